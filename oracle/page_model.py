@@ -1,0 +1,189 @@
+"""Exact model of the paged GCA cache: which page holds which row, step by step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The pages say the cache is paged so that the frequent appends and drops of a
+streaming window do not force re-allocation (deep dive §3.4; news article,
+inference paragraph), that a frame leaving the window keeps only its S
+summary rows ("compressing eviction", paper-to-code map §二 2.3) and that
+anchors stay (technical summary §2.2).  They do not give a page policy, so
+this model fixes one, and the device cache must reproduce it bit for bit:
+
+* The pool has ``num_pages`` pages of P token slots each.  A page is either
+  free or used.  Allocation always takes the lowest-numbered free page.
+* A full frame occupies ppf = ceil(F / P) pages of its own; its row r sits in
+  page ``pages[r // P]``, slot ``r % P``.  The last page of a frame has
+  F - (ppf-1)*P valid slots.
+* Anchor initialisation appends frames 0..n-1 in order, each taking ppf
+  pages in ascending order.
+* Step t appends frame t the same way.  Then, if t - k >= n, frame
+  e = t - k leaves the window: for r = 0..S-1 its summary row r is copied to
+  summary slot g = S*j + r, where j counts frames evicted before it; slot g
+  lives in page ``summary_pages[g // P]`` at position g % P, and a new
+  summary page (lowest free) is appended to that list when g // P reaches its
+  length.  Only after the copy are frame e's ppf pages freed.
+* Reset frees everything.
+
+Parity status: the policy is this repository's own specification, pinned by
+invariants (no page used twice, used + free = pool, resident rows equal the
+oracle's cached-token count, the closed form of the technical summary §2.4,
+and the computed peak pool size).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+
+def pages_per_frame(F: int, P: int) -> int:
+    return -(-F // P)
+
+
+def pool_pages_needed(n: int, k: int, F: int, S: int, P: int, max_frames: int) -> int:
+    """Peak page count over a stream of max_frames frames (simulated)."""
+    m = PageModel(n=n, k=k, F=F, S=S, P=P, num_pages=10 ** 9, max_frames=max_frames)
+    m.anchor_init()
+    for t in range(n, max_frames):
+        m.step(t)
+    return m.peak_used
+
+
+@dataclass
+class PageModel:
+    n: int
+    k: int
+    F: int
+    S: int
+    P: int
+    num_pages: int
+    max_frames: int
+    used: list = field(default_factory=list)  # sorted free-list is derived
+    frame_pages: dict = field(default_factory=dict)  # frame -> [pages]
+    summary_pages: list = field(default_factory=list)
+    summary_src: list = field(default_factory=list)  # slot g -> (frame, row)
+    n_traj: int = 0
+    n_frames: int = 0  # frames appended so far (next frame index)
+    peak_used: int = 0
+
+    def __post_init__(self):
+        self.ppf = pages_per_frame(self.F, self.P)
+        self._used = set()
+        self._free_hint = 0  # no page below this index is free
+
+    # -- allocator ---------------------------------------------------------
+    def _alloc(self) -> int:
+        p = self._free_hint
+        while p in self._used:
+            p += 1
+        if p >= self.num_pages:
+            raise MemoryError("page pool exhausted")
+        self._used.add(p)
+        self._free_hint = p + 1
+        self.peak_used = max(self.peak_used, len(self._used))
+        return p
+
+    def _free(self, p: int) -> None:
+        self._used.remove(p)
+        self._free_hint = min(self._free_hint, p)
+
+    @property
+    def used_pages(self) -> int:
+        return len(self._used)
+
+    def used_bitmap(self) -> list:
+        return [p in self._used for p in range(self.num_pages)]
+
+    # -- operations --------------------------------------------------------
+    def _append_frame(self, f: int) -> None:
+        if f >= self.max_frames:
+            raise ValueError("frame index beyond max_frames")
+        self.frame_pages[f] = [self._alloc() for _ in range(self.ppf)]
+        self.n_frames = f + 1
+
+    def anchor_init(self) -> None:
+        if self.n_frames != 0:
+            raise RuntimeError("anchor_init on a non-empty cache")
+        for f in range(self.n):
+            self._append_frame(f)
+
+    def _evict(self, e: int) -> None:
+        for r in range(self.S):
+            g = self.S * self.n_traj + r
+            if g // self.P >= len(self.summary_pages):
+                self.summary_pages.append(self._alloc())
+            self.summary_src.append((e, r))
+        for p in self.frame_pages.pop(e):
+            self._free(p)
+        self.n_traj += 1
+
+    def begin_step(self, t: int) -> None:
+        """Append frame t; the attention of step t reads the cache after this."""
+        if t != self.n_frames or t < self.n:
+            raise RuntimeError("steps must follow anchor init in frame order")
+        self._append_frame(t)
+
+    def end_step(self, t: int) -> None:
+        """Evict frame t-k to the trajectory memory if it leaves the window."""
+        if t - self.k >= self.n:
+            self._evict(t - self.k)
+
+    def step(self, t: int) -> None:
+        self.begin_step(t)
+        self.end_step(t)
+
+    def reset(self) -> None:
+        self._used.clear()
+        self._free_hint = 0
+        self.frame_pages.clear()
+        self.summary_pages.clear()
+        self.summary_src.clear()
+        self.n_traj = 0
+        self.n_frames = 0
+
+    # -- queries -----------------------------------------------------------
+    def frame_row_location(self, f: int, r: int):
+        pages = self.frame_pages[f]
+        return pages[r // self.P], r % self.P
+
+    def summary_location(self, g: int):
+        return self.summary_pages[g // self.P], g % self.P
+
+    def resident_locations(self) -> dict:
+        """(frame, row) -> (page, slot) for every cached row."""
+        out = {}
+        for f, pages in self.frame_pages.items():
+            for r in range(self.F):
+                out[(f, r)] = (pages[r // self.P], r % self.P)
+        for g, (f, r) in enumerate(self.summary_src):
+            out[(f, r)] = self.summary_location(g)
+        return out
+
+    def visible_page_list(self):
+        """Pages a query of the newest frame attends to, with valid counts.
+
+        Meaningful between ``begin_step`` and ``end_step`` (or right after
+        ``anchor_init``, where it lists the anchor pages).
+
+        Order: anchor frames, summary pages, window frames (oldest first),
+        current frame.  Valid count = number of leading slots holding rows.
+        """
+        t = self.n_frames - 1
+        out = []
+        last_valid = self.F - (self.ppf - 1) * self.P
+        for f in range(self.n):
+            for j, p in enumerate(self.frame_pages[f]):
+                out.append((p, self.P if j < self.ppf - 1 else last_valid))
+        ns = self.S * self.n_traj
+        for j, p in enumerate(self.summary_pages):
+            out.append((p, min(self.P, ns - j * self.P)))
+        for f in sorted(self.frame_pages):
+            if f < self.n:
+                continue
+            for j, p in enumerate(self.frame_pages[f]):
+                out.append((p, self.P if j < self.ppf - 1 else last_valid))
+        assert t == max(self.frame_pages)
+        return out
+
+
+def summary_pages_for(n_traj: int, S: int, P: int) -> int:
+    return math.ceil(S * n_traj / P)
