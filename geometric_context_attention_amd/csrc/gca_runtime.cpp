@@ -1,0 +1,509 @@
+// Host runtime of the GCA library: configuration checks, workspace layout,
+// call-order state, page-count prediction and kernel sequencing.
+//
+// Every cache decision is a deterministic function of the frame counter, so
+// the host predicts page use (and refuses a step that would exhaust the pool)
+// without reading anything back from the device.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gca.h"
+#include "gca_internal.h"
+
+using namespace gca;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(GCA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Derived sizes and workspace layout of a configuration.
+struct Geometry {
+  int F = 0, ppf = 0, pool = 0, words = 0, max_sum_pages = 0, f_last_valid = 0;
+  int64_t ftab_entries = 0;
+  size_t eb = 0;          // element bytes
+  size_t pool_bytes = 0;  // one pool (K or V) of one layer
+  size_t meta_bytes = 0;  // bitmap + ftab + slist + ctr of one layer
+  size_t part_o_bytes = 0, part_ml_bytes = 0;
+  size_t layer_stride = 0;
+  size_t total = 0;
+  float scale = 0.f;
+};
+
+int query_rows(const gca_config& c) { return c.dtype == GCA_FP32 ? 256 : kQBlock; }
+
+int choose_splits(const gca_config& c, int qblocks, int64_t npg) {
+  const int64_t base = (int64_t)c.num_heads * qblocks;
+  int64_t s = cdiv(kTargetWgs, base);
+  if (c.max_splits > 0 && s > c.max_splits) s = c.max_splits;
+  if (s > npg) s = npg;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int validate(const gca_config* c, std::string& why) {
+  if (c == nullptr) { why = "config is NULL"; return GCA_E_INVALID_ARG; }
+  if (c->num_layers < 1) { why = "num_layers must be >= 1"; return GCA_E_INVALID_ARG; }
+  if (c->num_heads < 1 || c->num_heads > 4096) { why = "num_heads must be in [1, 4096]"; return GCA_E_INVALID_ARG; }
+  if (c->head_dim < 1) { why = "head_dim must be >= 1"; return GCA_E_INVALID_ARG; }
+  if (c->head_dim != kHeadDim) { why = "only head_dim 64 is supported"; return GCA_E_UNSUPPORTED; }
+  if (c->image_tokens < 1) { why = "image_tokens must be >= 1"; return GCA_E_INVALID_ARG; }
+  if (c->summary_tokens < 1 || c->summary_tokens > kPage) {
+    why = "summary_tokens must be in [1, 64]"; return GCA_E_INVALID_ARG;
+  }
+  if (c->image_tokens > (1 << 20)) { why = "image_tokens too large"; return GCA_E_INVALID_ARG; }
+  if (c->n_anchor < 1) { why = "n_anchor must be >= 1"; return GCA_E_INVALID_ARG; }
+  if (c->k_window < 0) { why = "k_window must be >= 0"; return GCA_E_INVALID_ARG; }
+  if (c->max_frames < c->n_anchor) { why = "max_frames must be >= n_anchor"; return GCA_E_INVALID_ARG; }
+  if (c->page_tokens != kPage) { why = "only page_tokens 64 is supported"; return GCA_E_UNSUPPORTED; }
+  if (c->dtype != GCA_BF16 && c->dtype != GCA_FP32) { why = "dtype must be GCA_BF16 or GCA_FP32"; return GCA_E_INVALID_ARG; }
+  if (!(std::isfinite(c->scale) && c->scale >= 0.f)) { why = "scale must be finite and >= 0"; return GCA_E_INVALID_ARG; }
+  if (c->pool_pages < 0) { why = "pool_pages must be >= 0"; return GCA_E_INVALID_ARG; }
+  if (c->max_splits < 0) { why = "max_splits must be >= 0"; return GCA_E_INVALID_ARG; }
+  const int64_t F = (int64_t)c->image_tokens + c->summary_tokens;
+  if ((int64_t)c->n_anchor * F > (1 << 24)) { why = "anchor block too large"; return GCA_E_INVALID_ARG; }
+  const int64_t ppf = cdiv(F, kPage);
+  if ((int64_t)c->max_frames * ppf > (1LL << 30)) { why = "max_frames too large"; return GCA_E_INVALID_ARG; }
+  return GCA_OK;
+}
+
+// Peak pages of a max_frames stream: anchors + window + current frame +
+// summary pages at the last eviction (the tail page is taken before the
+// evicted frame's pages are freed).
+int64_t peak_pages(const gca_config& c, int ppf) {
+  const int64_t n = c.n_anchor, k = c.k_window, T = c.max_frames;
+  const int64_t wmax = std::min<int64_t>(k, T - 1 - n);  // -1 when T == n
+  const int64_t full = (n + wmax + 1) * ppf;
+  const int64_t traj = std::max<int64_t>(0, T - n - k);
+  return full + cdiv(traj * c.summary_tokens, kPage);
+}
+
+void make_geometry(const gca_config& c, Geometry& g) {
+  g.F = c.image_tokens + c.summary_tokens;
+  g.ppf = (int)cdiv(g.F, kPage);
+  g.f_last_valid = g.F - (g.ppf - 1) * kPage;
+  const int64_t peak = peak_pages(c, g.ppf);
+  g.pool = c.pool_pages > 0 ? c.pool_pages : (int)peak;
+  g.words = (int)cdiv(g.pool, 32);
+  const int64_t traj_max = std::max<int64_t>(0, (int64_t)c.max_frames - c.n_anchor - c.k_window);
+  g.max_sum_pages = (int)std::max<int64_t>(1, cdiv(traj_max * c.summary_tokens, kPage));
+  g.ftab_entries = (int64_t)c.max_frames * g.ppf;
+  g.eb = c.dtype == GCA_FP32 ? 4 : 2;
+  const size_t page_bytes = (size_t)c.num_heads * kPage * kHeadDim * g.eb;
+  g.pool_bytes = align256((size_t)g.pool * page_bytes);
+  g.meta_bytes = align256((size_t)g.words * 4) + align256((size_t)g.ftab_entries * 4) +
+                 align256((size_t)g.max_sum_pages * 4) + align256(kCtrCount * 4);
+  g.layer_stride = 2 * g.pool_bytes + g.meta_bytes;
+  // split-K scratch, sized for the larger of the anchor block and a step
+  const int qr = query_rows(c);
+  size_t po = 0, pml = 0;
+  const int64_t lq[2] = {(int64_t)c.n_anchor * g.F, g.F};
+  for (int64_t L : lq) {
+    const int qb = (int)cdiv(L, qr);
+    const int64_t lq_pad = cdiv(L, kQBlock) * kQBlock;
+    const int s = choose_splits(c, qb, INT32_MAX);
+    if (s > 1) {
+      po = std::max(po, (size_t)c.num_heads * s * lq_pad * kHeadDim * 4);
+      pml = std::max(pml, (size_t)c.num_heads * s * lq_pad * 8);
+    }
+  }
+  g.part_o_bytes = align256(po);
+  g.part_ml_bytes = align256(pml);
+  g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes;
+  g.scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
+}
+
+struct LayerHost {
+  bool streaming = false;
+  int frames = 0;  // frames appended
+  int traj = 0;    // frames in trajectory memory
+  int used = 0;    // pages in use
+};
+
+struct EventPair {
+  hipEvent_t a = nullptr, b = nullptr;
+  double flop = 0, bytes = 0;
+  bool pending = false;
+};
+
+}  // namespace
+
+struct gca_ctx {
+  gca_config cfg;
+  Geometry g;
+  char* ws = nullptr;
+  std::vector<LayerDev> dev;
+  std::vector<LayerHost> host;
+  float* part_o = nullptr;
+  float2* part_ml = nullptr;
+  bool f32 = false;
+  // profiling
+  bool prof = false;
+  std::vector<EventPair> ev;
+  size_t ev_next = 0;
+  double attn_ms = 0, attn_flop = 0, attn_bytes = 0;
+  int64_t attn_launches = 0;
+};
+
+namespace {
+
+int harvest(gca_ctx* c, EventPair& e) {
+  if (!e.pending) return GCA_OK;
+  hipError_t r = hipEventSynchronize(e.b);
+  if (r != hipSuccess) return hip_fail(r, "hipEventSynchronize");
+  float ms = 0.f;
+  r = hipEventElapsedTime(&ms, e.a, e.b);
+  if (r != hipSuccess) return hip_fail(r, "hipEventElapsedTime");
+  c->attn_ms += ms;
+  c->attn_flop += e.flop;
+  c->attn_bytes += e.bytes;
+  c->attn_launches += 1;
+  e.pending = false;
+  return GCA_OK;
+}
+
+// Launch attention (+ merge) over the page list `pl` for `Lq` query rows.
+int run_attention(gca_ctx* c, int layer, const void* q, void* out, float* lse, int Lq,
+                  const PageList& pl, int64_t keys, hipStream_t st) {
+  const gca_config& cfg = c->cfg;
+  AttnArgs a{};
+  a.q = q;
+  a.kpool = c->dev[layer].kpool;
+  a.vpool = c->dev[layer].vpool;
+  a.ftab = c->dev[layer].ftab;
+  a.slist = c->dev[layer].slist;
+  a.pl = pl;
+  a.Lq = Lq;
+  a.H = cfg.num_heads;
+  a.qblocks = (int)cdiv(Lq, query_rows(cfg));
+  const int64_t npg = (int64_t)pl.a_cnt + pl.s_cnt + pl.w_cnt;
+  a.nsplit = choose_splits(cfg, a.qblocks, npg);
+  a.scale = c->g.scale;
+  a.scale_log2 = (float)(c->g.scale * 1.4426950408889634);
+  a.out = out;
+  a.lse = lse;
+  a.part_o = c->part_o;
+  a.part_ml = c->part_ml;
+  a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
+  a.pool = c->g.pool;
+  EventPair* ep = nullptr;
+  if (c->prof) {
+    ep = &c->ev[c->ev_next];
+    c->ev_next = (c->ev_next + 1) % c->ev.size();
+    int rc = harvest(c, *ep);
+    if (rc != GCA_OK) return rc;
+    hipError_t r = hipEventRecord(ep->a, st);
+    if (r != hipSuccess) return hip_fail(r, "hipEventRecord");
+  }
+  hipError_t e = launch_attention(a, c->f32, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (ep != nullptr) {
+    hipError_t r = hipEventRecord(ep->b, st);
+    if (r != hipSuccess) return hip_fail(r, "hipEventRecord");
+    ep->flop = 4.0 * Lq * (double)keys * cfg.head_dim * cfg.num_heads;
+    ep->bytes = 2.0 * (double)keys * cfg.num_heads * cfg.head_dim * c->g.eb;
+    ep->pending = true;
+  }
+  if (a.nsplit > 1) {
+    e = launch_merge(a, c->f32, st);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
+  return GCA_OK;
+}
+
+int check_ctx_layer(gca_ctx* c, int layer) {
+  if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  if (layer < 0 || layer >= c->cfg.num_layers) return fail(GCA_E_INVALID_ARG, "layer out of range");
+  return GCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gca_workspace_bytes(const gca_config* cfg) {
+  std::string why;
+  if (validate(cfg, why) != GCA_OK) {
+    g_err = why;
+    return 0;
+  }
+  Geometry g;
+  make_geometry(*cfg, g);
+  return g.total;
+}
+
+int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* stream,
+               gca_ctx** out) {
+  std::string why;
+  int rc = validate(cfg, why);
+  if (rc != GCA_OK) return fail(rc, why);
+  if (out == nullptr) return fail(GCA_E_INVALID_ARG, "out is NULL");
+  if (dev_workspace == nullptr) return fail(GCA_E_INVALID_ARG, "workspace is NULL");
+  if (((uintptr_t)dev_workspace & 255) != 0) return fail(GCA_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  Geometry g;
+  make_geometry(*cfg, g);
+  if (bytes < g.total) return fail(GCA_E_INVALID_ARG, "workspace too small: need " + std::to_string(g.total) + " bytes");
+  if (cfg->pool_pages == 0 && g.pool < (int64_t)cfg->n_anchor * g.ppf)
+    return fail(GCA_E_INVALID_ARG, "pool smaller than the anchor block");
+  gca_ctx* c = new gca_ctx();
+  c->cfg = *cfg;
+  c->g = g;
+  c->ws = (char*)dev_workspace;
+  c->f32 = cfg->dtype == GCA_FP32;
+  c->dev.resize(cfg->num_layers);
+  c->host.resize(cfg->num_layers);
+  for (int l = 0; l < cfg->num_layers; ++l) {
+    char* base = c->ws + g.layer_stride * l;
+    LayerDev& d = c->dev[l];
+    d.kpool = base;
+    d.vpool = base + g.pool_bytes;
+    char* m = base + 2 * g.pool_bytes;
+    d.bitmap = (uint32_t*)m;
+    m += align256((size_t)g.words * 4);
+    d.ftab = (int32_t*)m;
+    m += align256((size_t)g.ftab_entries * 4);
+    d.slist = (int32_t*)m;
+    m += align256((size_t)g.max_sum_pages * 4);
+    d.ctr = (int32_t*)m;
+  }
+  char* tail = c->ws + g.layer_stride * cfg->num_layers;
+  c->part_o = g.part_o_bytes ? (float*)tail : nullptr;
+  c->part_ml = g.part_ml_bytes ? (float2*)(tail + g.part_o_bytes) : nullptr;
+  rc = gca_reset(c, stream);
+  if (rc != GCA_OK) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return GCA_OK;
+}
+
+int gca_reset(gca_ctx* c, void* stream) {
+  if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  for (int l = 0; l < c->cfg.num_layers; ++l) {
+    hipError_t e = launch_reset(c->dev[l], c->g.words, (int)c->g.ftab_entries, c->g.max_sum_pages, st);
+    if (e != hipSuccess) return hip_fail(e, "reset launch");
+    c->host[l] = LayerHost{};
+  }
+  return GCA_OK;
+}
+
+int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v,
+                    void* out, float* lse, void* stream) {
+  int rc = check_ctx_layer(c, layer);
+  if (rc != GCA_OK) return rc;
+  if (!q || !k || !v || !out) return fail(GCA_E_INVALID_ARG, "q, k, v and out must be non-NULL");
+  LayerHost& hs = c->host[layer];
+  if (hs.streaming || hs.frames != 0) return fail(GCA_E_BAD_STATE, "anchor_init on a layer that is not empty");
+  const gca_config& cfg = c->cfg;
+  const Geometry& g = c->g;
+  const int need = cfg.n_anchor * g.ppf;
+  if (need > g.pool) return fail(GCA_E_OUT_OF_PAGES, "pool cannot hold the anchor frames");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_alloc_frames(c->dev[layer], g.pool, g.ppf, 0, cfg.n_anchor, st);
+  if (e != hipSuccess) return hip_fail(e, "alloc launch");
+  e = launch_append(c->dev[layer], k, v, 0, cfg.n_anchor, g.ppf, g.F, cfg.num_heads, c->f32, st);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  PageList pl{};
+  pl.a_cnt = need;
+  pl.s_cnt = 0;
+  pl.s_last_valid = kPage;
+  pl.w_first = 0;
+  pl.w_cnt = 0;
+  pl.ppf = g.ppf;
+  pl.f_last_valid = g.f_last_valid;
+  const int Lq = cfg.n_anchor * g.F;
+  rc = run_attention(c, layer, q, out, lse, Lq, pl, (int64_t)Lq, st);
+  if (rc != GCA_OK) return rc;
+  hs.streaming = true;
+  hs.frames = cfg.n_anchor;
+  hs.used = need;
+  hs.traj = 0;
+  return GCA_OK;
+}
+
+int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
+             float* lse, void* stream) {
+  int rc = check_ctx_layer(c, layer);
+  if (rc != GCA_OK) return rc;
+  if (!q || !k || !v || !out) return fail(GCA_E_INVALID_ARG, "q, k, v and out must be non-NULL");
+  LayerHost& hs = c->host[layer];
+  if (!hs.streaming) return fail(GCA_E_BAD_STATE, "step before anchor_init");
+  const gca_config& cfg = c->cfg;
+  const Geometry& g = c->g;
+  const int n = cfg.n_anchor, kw = cfg.k_window, S = cfg.summary_tokens;
+  const int t = hs.frames;
+  if (t >= cfg.max_frames) return fail(GCA_E_OUT_OF_PAGES, "stream reached max_frames; reset first");
+  const int w = std::min(kw, t - n);
+  const bool evict = (int64_t)t - kw >= n;
+  const int nsp = (int)cdiv((int64_t)S * hs.traj, kPage);
+  const int new_sum = evict ? (int)(cdiv((int64_t)S * (hs.traj + 1), kPage) - nsp) : 0;
+  if ((int64_t)hs.used + g.ppf + new_sum > g.pool)
+    return fail(GCA_E_OUT_OF_PAGES, "page pool exhausted at frame " + std::to_string(t));
+  hipStream_t st = (hipStream_t)stream;
+  const LayerDev& d = c->dev[layer];
+  hipError_t e = launch_alloc_frames(d, g.pool, g.ppf, t, 1, st);
+  if (e != hipSuccess) return hip_fail(e, "alloc launch");
+  e = launch_append(d, k, v, t, 1, g.ppf, g.F, cfg.num_heads, c->f32, st);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  PageList pl{};
+  pl.a_cnt = n * g.ppf;
+  pl.s_cnt = nsp;
+  pl.s_last_valid = nsp > 0 ? (int)((int64_t)S * hs.traj - (int64_t)(nsp - 1) * kPage) : kPage;
+  pl.w_first = (t - w) * g.ppf;
+  pl.w_cnt = (w + 1) * g.ppf;
+  pl.ppf = g.ppf;
+  pl.f_last_valid = g.f_last_valid;
+  const int64_t keys = (int64_t)(n + w + 1) * g.F + (int64_t)S * hs.traj;
+  rc = run_attention(c, layer, q, out, lse, g.F, pl, keys, st);
+  if (rc != GCA_OK) return rc;
+  if (evict) {
+    e = launch_evict(d, g.pool, t - kw, g.ppf, S, cfg.num_heads, c->f32, st);
+    if (e != hipSuccess) return hip_fail(e, "evict launch");
+  }
+  hs.frames = t + 1;
+  hs.used += g.ppf;
+  if (evict) {
+    hs.used += new_sum - g.ppf;
+    hs.traj += 1;
+  }
+  return GCA_OK;
+}
+
+void gca_destroy(gca_ctx* c) {
+  if (c == nullptr) return;
+  for (EventPair& e : c->ev) {
+    if (e.a) hipEventDestroy(e.a);
+    if (e.b) hipEventDestroy(e.b);
+  }
+  delete c;
+}
+
+const char* gca_last_error(void) { return g_err.c_str(); }
+
+int gca_plan(const gca_config* cfg, int32_t t, gca_plan_info* out) {
+  std::string why;
+  int rc = validate(cfg, why);
+  if (rc != GCA_OK) return fail(rc, why);
+  if (out == nullptr) return fail(GCA_E_INVALID_ARG, "out is NULL");
+  if (t < 0 || t >= cfg->max_frames) return fail(GCA_E_INVALID_ARG, "t out of range");
+  Geometry g;
+  make_geometry(*cfg, g);
+  const int64_t n = cfg->n_anchor, k = cfg->k_window, S = cfg->summary_tokens, F = g.F;
+  gca_plan_info p{};
+  int64_t Lq, npg;
+  if (t < n) {
+    Lq = n * F;
+    p.keys = n * F;
+    p.cached_after = n * F;
+    npg = n * g.ppf;
+    p.used_pages_after = (int32_t)(n * g.ppf);
+  } else {
+    Lq = F;
+    const int64_t w = std::min<int64_t>(k, t - n);
+    const int64_t traj = std::max<int64_t>(0, t - n - k);
+    p.keys = (n + w + 1) * F + S * traj;
+    npg = n * g.ppf + cdiv(S * traj, kPage) + (w + 1) * g.ppf;
+    const int64_t wa = std::min<int64_t>(k, t - n + 1);
+    const int64_t traj_after = t + 1 - n - wa;
+    p.cached_after = (n + wa) * F + S * traj_after;
+    p.used_pages_after = (int32_t)((n + wa) * g.ppf + cdiv(S * traj_after, kPage));
+  }
+  p.pages_visible = (int32_t)npg;
+  p.pool_pages = g.pool;
+  p.pages_per_frame = g.ppf;
+  p.qblocks = (int32_t)cdiv(Lq, query_rows(*cfg));
+  p.splits = choose_splits(*cfg, p.qblocks, npg);
+  p.flop = 4.0 * (double)Lq * (double)p.keys * cfg->head_dim * cfg->num_heads;
+  *out = p;
+  return GCA_OK;
+}
+
+int gca_export_state(gca_ctx* c, int32_t layer, gca_state_host* dst, void* stream) {
+  int rc = check_ctx_layer(c, layer);
+  if (rc != GCA_OK) return rc;
+  if (dst == nullptr) return fail(GCA_E_INVALID_ARG, "dst is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  const LayerDev& d = c->dev[layer];
+  int32_t ctr[kCtrCount];
+  hipError_t e = hipMemcpyAsync(ctr, d.ctr, sizeof(ctr), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && dst->used_bitmap)
+    e = hipMemcpyAsync(dst->used_bitmap, d.bitmap, (size_t)c->g.words * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && dst->frame_table)
+    e = hipMemcpyAsync(dst->frame_table, d.ftab, (size_t)c->g.ftab_entries * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess && dst->summary_pages)
+    e = hipMemcpyAsync(dst->summary_pages, d.slist, (size_t)c->g.max_sum_pages * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e, "export_state copy");
+  dst->frames_appended = ctr[kCtrFrames];
+  dst->n_traj = ctr[kCtrTraj];
+  dst->n_summary_pages = ctr[kCtrSumPages];
+  dst->used_pages = ctr[kCtrUsed];
+  dst->device_error = ctr[kCtrError];
+  dst->pool_pages = c->g.pool;
+  dst->pages_per_frame = c->g.ppf;
+  dst->max_frames = c->cfg.max_frames;
+  dst->max_summary_pages = c->g.max_sum_pages;
+  return GCA_OK;
+}
+
+int gca_pool_views(gca_ctx* c, int32_t layer, void** k_pool, void** v_pool, size_t* page_bytes) {
+  int rc = check_ctx_layer(c, layer);
+  if (rc != GCA_OK) return rc;
+  if (k_pool) *k_pool = c->dev[layer].kpool;
+  if (v_pool) *v_pool = c->dev[layer].vpool;
+  if (page_bytes) *page_bytes = (size_t)c->cfg.num_heads * kPage * kHeadDim * c->g.eb;
+  return GCA_OK;
+}
+
+int gca_profile_enable(gca_ctx* c, int32_t on) {
+  if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  if (on) {
+    if (c->ev.empty()) {
+      c->ev.resize(2048);
+      for (EventPair& e : c->ev) {
+        hipError_t r = hipEventCreate(&e.a);
+        if (r == hipSuccess) r = hipEventCreate(&e.b);
+        if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+      }
+    }
+    for (EventPair& e : c->ev) e.pending = false;
+    c->attn_ms = c->attn_flop = c->attn_bytes = 0;
+    c->attn_launches = 0;
+  }
+  c->prof = on != 0;
+  return GCA_OK;
+}
+
+int gca_profile_read(gca_ctx* c, gca_profile* out) {
+  if (c == nullptr || out == nullptr) return fail(GCA_E_INVALID_ARG, "NULL argument");
+  for (EventPair& e : c->ev) {
+    int rc = harvest(c, e);
+    if (rc != GCA_OK) return rc;
+  }
+  out->attn_ms = c->attn_ms;
+  out->attn_launches = c->attn_launches;
+  out->attn_flop = c->attn_flop;
+  out->attn_kv_bytes = c->attn_bytes;
+  return GCA_OK;
+}
+
+}  // extern "C"
