@@ -1,0 +1,251 @@
+"""Benchmark of the GCA step on one MI355X.
+
+One bench step = one whole stream of the direct-mode stack: reset, anchor
+initialisation of the 12 layers, then frames n..T-1 streamed one per step
+through all 12 layers (M = 500 image + 6 summary tokens, 16 heads, head_dim
+64, n = 3 anchors, window k = 64, T = 10000 frames, bf16 in / fp32
+accumulate).  Reported value: frames per second of the whole stream.
+
+Inputs are synthetic (seeded N(0,1)) and resident in HBM before timing: each
+layer draws a pool of 64 distinct frames and frame t uses entry
+(t + 17*layer) mod 64.  The kernels do the same work whatever the values.
+
+The JSON line also carries:
+* roofline: the attention kernel (the dominant one) against the dense bf16
+  MFMA peak, from HIP events around every attention launch of the timed
+  region (algorithmic flop 4 * (M+6) * keys * D * H per launch);
+* cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
+  workload (one layer, a few sampled steps, linear in the key count) and
+  extrapolated to the whole stream.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "GCA frames/s (12 layers, M=500,n=3,k=64,T=10k) + % of bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1, help="timed streams")
+    ap.add_argument("--warmup", type=int, default=1, help="untimed streams before timing")
+    ap.add_argument("--frames", type=int, default=10000, help="T (frames per stream)")
+    ap.add_argument("--layers", type=int, default=12)
+    ap.add_argument("--window", type=int, default=64)
+    ap.add_argument("--image-tokens", type=int, default=500)
+    ap.add_argument("--pool", type=int, default=64, help="resident input frames per layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the GCA step is built and timed on a single MI355X; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from geometric_context_attention_amd import _lib as G
+    from geometric_context_attention_amd.synth import StreamSpec, draw_frames
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H, D, M, S, n = 16, 64, args.image_tokens, 6, 3
+    k, T, Ly = args.window, args.frames, args.layers
+    F = M + S
+    cfg = G.make_config(num_layers=Ly, num_heads=H, head_dim=D, image_tokens=M, summary_tokens=S,
+                        n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_BF16)
+    stack = G.GcaStack(cfg, device=dev)
+    L = G.lib()
+    ctx = stack.ctx
+    log(f"workspace {stack.workspace.numel() / 2**30:.2f} GiB, pool "
+        f"{G.gca_plan(cfg, 0)['pool_pages']} pages per layer")
+
+    # resident inputs
+    R = args.pool
+    pools = []
+    for layer in range(Ly):
+        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=32)
+        q, kk, v = draw_frames(spec, layer, 0, max(R, n), device=dev)
+        pools.append((q, kk, v))
+    outs = [torch.empty((F, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Ly)]
+    anc_out = torch.empty((n * F, H, D), dtype=torch.bfloat16, device=dev)
+    # per layer, per pool entry: device addresses
+    ptrs = []
+    for layer in range(Ly):
+        q, kk, v = pools[layer]
+        fb = F * H * D * 2
+        ptrs.append([(ctypes.c_void_p(q.data_ptr() + i * fb), ctypes.c_void_p(kk.data_ptr() + i * fb),
+                      ctypes.c_void_p(v.data_ptr() + i * fb)) for i in range(R)])
+    optr = [ctypes.c_void_p(o.data_ptr()) for o in outs]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    step_fn = L.gca_step
+    anchor_fn = L.gca_anchor_init
+
+    def run_stream():
+        rc = L.gca_reset(ctx, sp)
+        if rc:
+            raise G.GcaError(rc, L.gca_last_error().decode())
+        for layer in range(Ly):
+            q, kk, v = pools[layer]
+            rc = anchor_fn(ctx, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kk.data_ptr()),
+                           ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(anc_out.data_ptr()), None, sp)
+            if rc:
+                raise G.GcaError(rc, L.gca_last_error().decode())
+        for t in range(n, T):
+            for layer in range(Ly):
+                qp, kp, vp = ptrs[layer][(t + 17 * layer) % R]
+                rc = step_fn(ctx, layer, qp, kp, vp, optr[layer], None, sp)
+                if rc:
+                    raise G.GcaError(rc, L.gca_last_error().decode())
+            if t % 2000 == 0:
+                log(f"  frame {t}")
+
+    for w in range(args.warmup):
+        log(f"warmup stream {w + 1}/{args.warmup}")
+        run_stream()
+    torch.cuda.synchronize()
+    G.gca_profile_enable(ctx, True)
+    log(f"timed: {args.steps} stream(s) of {T} frames x {Ly} layers")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_stream()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = G.gca_profile_read(ctx)
+    G.gca_profile_enable(ctx, False)
+    frames = args.steps * T
+    fps = frames / elapsed
+    attn_avg_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
+    achieved = prof["attn_flop"] / (prof["attn_ms"] * 1e-3) / 1e12 if prof["attn_ms"] > 0 else 0.0
+    log(f"{fps:.1f} frames/s; attention {prof['attn_launches']} launches, avg {attn_avg_ms * 1e3:.1f} us, "
+        f"{achieved:.1f} TFLOP/s; attention share of wall {prof['attn_ms'] / 1e3 / elapsed:.2%}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(fps, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), resident pool of 64 frames per layer)",
+        "config": {"workload": f"GCA direct-mode stream: {Ly} layers, H={H}, D={D}, M={M}+{S}, "
+                               f"n={n}, k={k}, T={T}, keyframe interval 1, bf16",
+                   "layers": Ly, "heads": H, "head_dim": D, "image_tokens": M,
+                   "summary_tokens": S, "n_anchor": n, "k_window": k, "frames": T},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_attn_bf16",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(attn_avg_ms * 1e3, 2),
+            "launches": prof["attn_launches"],
+            "algorithmic_flop_per_launch": prof["attn_flop"] / max(prof["attn_launches"], 1),
+            "algorithmic_kv_bytes_per_launch": prof["attn_kv_bytes"] / max(prof["attn_launches"], 1),
+        },
+    }
+    stack.close()
+    del pools
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, H, D, M, S, n, k, T, Ly)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
+    """Time the fp64 oracle on sampled steps of one layer; extrapolate.
+
+    The oracle's step cost is linear in the key count; time(t) = a + b*keys(t)
+    is fitted to the samples and summed over the stream, times the layers.
+    """
+    import numpy as np
+    import torch
+
+    from geometric_context_attention_amd.synth import StreamSpec, draw_frames
+    from oracle import gca_oracle as go
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    shp = go.GcaShape(M=M, n=n, k=k, S=S)
+    F = M + S
+    R = 16
+    spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=16)
+    q, kk, v = (x.double().numpy() for x in draw_frames(spec, 0, 0, R))
+
+    def get_rows(f, rows):
+        return kk[f % R][rows], v[f % R][rows]
+
+    scale = 1 / math.sqrt(D)
+    samples = []
+    budget = args.cpu_seconds
+    spent = 0.0
+    t_a = time.perf_counter()
+    go.anchor_init(q[:n].reshape(n * F, H, D), kk[:n].reshape(n * F, H, D), v[:n].reshape(n * F, H, D), scale)
+    anchor_s = time.perf_counter() - t_a
+    spent += anchor_s
+    for t in (n + k, T // 4, T // 2, T - 1, n + 1):
+        if spent > budget and len(samples) >= 2:
+            break
+        t = min(max(t, n), T - 1)
+        t0 = time.perf_counter()
+        go.step(t, q[t % R], get_rows, shp, scale)
+        dt = time.perf_counter() - t0
+        spent += dt
+        samples.append((go.visible_key_count(t, shp), dt, t))
+        log(f"cpu oracle step t={t}: {dt:.2f} s")
+    keys = np.array([s[0] for s in samples], dtype=float)
+    secs = np.array([s[1] for s in samples])
+    b, a = np.polyfit(keys, secs, 1) if len(samples) >= 2 else (secs[0] / keys[0], 0.0)
+    all_keys = np.array([go.visible_key_count(t, shp) if t < n + k + 2 else
+                         M * (n + k + 1) + S * (t + 1) for t in range(n, T)], dtype=float)
+    stream_s = Ly * (anchor_s + float(np.sum(a + b * all_keys)))
+    return {
+        "value": round(T / stream_s, 6),
+        "unit": "frames/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, one layer: anchor init + steps t={[s[2] for s in samples]} "
+                   f"({spent:.1f} s); time linear in keys fitted and summed over t={n}..{T - 1}, "
+                   f"x{Ly} layers (extrapolated)"),
+    }
+
+
+if __name__ == "__main__":
+    main()
