@@ -8,8 +8,10 @@ namespace gca {
 
 constexpr int kPage = 64;        // token slots per page
 constexpr int kHeadDim = 64;     // head dimension the kernels are written for
-constexpr int kQBlock = 512;     // query rows per attention workgroup (8 waves x 64)
+constexpr int kQBlock = 512;     // query rows per bf16 attention workgroup (8 waves x 64)
+constexpr int kF32Rows = 256;    // query rows per fp32 attention workgroup
 constexpr int kTargetWgs = 256;  // one workgroup per MI355X compute unit
+constexpr int kMaxFramePages = 32;  // pages of one frame passed by value (F <= 2048)
 
 // Device-side state of one layer's cache, carved from the workspace.
 struct LayerDev {
@@ -30,28 +32,44 @@ enum Ctr : int {
   kCtrCount = 8
 };
 
-// The page list attention walks: ftab[0..a_cnt) ++ slist[0..s_cnt) ++
-// ftab[w_first .. w_first + w_cnt), entries of ftab being per frame-page.
+// Page ids of one frame, passed by value.
+struct FramePages {
+  int32_t p[kMaxFramePages];
+};
+
+// The page list attention walks, in logical order:
+//   ftab[0 .. a_cnt)                       anchor frame pages
+//   slist[0 .. s_cnt)                      summary pages (trajectory memory)
+//   ftab[w_first .. w_first + w_cnt)       window frame pages
+//   fresh.p[0 .. fresh_cnt)                pages of the frame being appended,
+//                                          filled from k_in / v_in on the way
 struct PageList {
-  int32_t a_cnt;        // anchor page entries (n * ppf)
-  int32_t s_cnt;        // summary pages
-  int32_t s_last_valid; // valid slots of the last summary page
-  int32_t w_first;      // first ftab entry of the window + current frames
-  int32_t w_cnt;        // window + current page entries
-  int32_t ppf;          // pages per frame
-  int32_t f_last_valid; // valid slots of a frame's last page
+  int32_t a_cnt;
+  int32_t s_cnt;
+  int32_t s_last_valid;  // valid slots of the last summary page
+  int32_t w_first;
+  int32_t w_cnt;
+  int32_t fresh_cnt;     // 0 or ppf
+  int32_t ppf;           // pages per frame
+  int32_t f_last_valid;  // valid slots of a frame's last page
 };
 
 struct AttnArgs {
   const void* q;        // [Lq][H][D]
-  const void* kpool;
-  const void* vpool;
+  void* kpool;
+  void* vpool;
   const int32_t* ftab;
   const int32_t* slist;
   PageList pl;
+  FramePages fresh;     // page ids of the appended frame
+  const void* k_in;     // [F][H][D] rows of the appended frame (fresh_cnt > 0)
+  const void* v_in;
+  int32_t fresh_frame;  // its frame index
+  LayerDev L;           // for the bookkeeping of the append (workgroup 0)
   int32_t Lq;
   int32_t H;
-  int32_t qblocks;      // ceil(Lq / 512)
+  int32_t F;            // rows per frame
+  int32_t qblocks;      // query blocks of the kernel's block size
   int32_t nsplit;
   float scale;          // softmax scale
   float scale_log2;     // scale * log2(e)
@@ -64,16 +82,32 @@ struct AttnArgs {
   int32_t pool;         // pages in the pool (entries outside [0, pool) are masked)
 };
 
+// Moving frame `frame` (pages `src`) into the trajectory memory: its S
+// summary rows go to summary slots g0 .. g0+S-1; slot g lives in page
+// `tail_page` when g / 64 == tail_index, else in `new_page` (a page that
+// starts zero-filled and is appended to the summary list at index
+// new_index).  Then the frame's pages are freed.
+struct EvictPlan {
+  FramePages src;
+  int32_t frame;
+  int32_t ppf;
+  int32_t S;
+  int32_t g0;
+  int32_t tail_page;   // -1 if the summary list is empty
+  int32_t tail_index;  // index of tail_page in the summary list
+  int32_t new_page;    // -1 if no page is needed
+  int32_t new_index;
+};
+
 // Launch wrappers (gca_kernels.hip).  All return hipGetLastError() after launch.
 hipError_t launch_reset(const LayerDev& L, int pool_words, int ftab_entries, int slist_entries,
                         hipStream_t st);
-hipError_t launch_alloc_frames(const LayerDev& L, int pool_pages, int ppf, int first_frame,
-                               int nframes, hipStream_t st);
-hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int first_frame,
-                         int nframes, int ppf, int F, int H, bool f32, hipStream_t st);
+hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int frame,
+                         const FramePages& pages, int ppf, int F, int H, bool f32,
+                         hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st);
-hipError_t launch_merge(const AttnArgs& a, bool f32, hipStream_t st);
-hipError_t launch_evict(const LayerDev& L, int pool_pages, int frame, int ppf, int S, int H,
-                        bool f32, hipStream_t st);
+// Merge of the key splits (when a.nsplit > 1) and the eviction (when ev != null),
+// in one launch.
+hipError_t launch_merge_evict(const AttnArgs& a, const EvictPlan* ev, bool f32, hipStream_t st);
 
 }  // namespace gca

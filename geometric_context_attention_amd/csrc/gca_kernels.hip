@@ -18,6 +18,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "gca_internal.h"
 
 namespace gca {
@@ -42,79 +44,22 @@ __global__ void k_reset(LayerDev L, int pool_words, int ftab_entries, int slist_
   if (i < kCtrCount) L.ctr[i] = 0;
 }
 
-// One workgroup: take the ppf*nframes lowest free pages; frame first_frame+f
-// gets ranks [f*ppf, (f+1)*ppf) in ascending page order.
-__global__ __launch_bounds__(1024) void k_alloc_frames(LayerDev L, int pool_pages, int ppf,
-                                                       int first_frame, int nframes) {
-  const int need = ppf * nframes;
-  const int nwords = (pool_pages + 31) >> 5;
-  __shared__ int s_scan[1024];
-  __shared__ int s_base;
-  if (threadIdx.x == 0) s_base = 0;
-  __syncthreads();
-  for (int w0 = 0; w0 < nwords; w0 += 1024) {
-    const int base = s_base;
-    if (base >= need) break;  // uniform: read after a barrier
-    const int w = w0 + (int)threadIdx.x;
-    uint32_t word = 0u, freebits = 0u;
-    if (w < nwords) {
-      word = L.bitmap[w];
-      const int tail = pool_pages & 31;
-      const uint32_t valid = (w == nwords - 1 && tail) ? ((1u << tail) - 1u) : 0xffffffffu;
-      freebits = ~word & valid;
-    }
-    const int cnt = __popc(freebits);
-    s_scan[threadIdx.x] = cnt;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = (int)threadIdx.x >= off ? s_scan[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_scan[threadIdx.x] += v;
-      __syncthreads();
-    }
-    const int incl = s_scan[threadIdx.x];
-    int rank = base + incl - cnt;
-    uint32_t taken = 0u;
-    while (freebits && rank < need) {
-      const int b = __ffs(freebits) - 1;
-      freebits &= freebits - 1u;
-      const int page = w * 32 + b;
-      L.ftab[(first_frame + rank / ppf) * ppf + rank % ppf] = page;
-      taken |= 1u << b;
-      ++rank;
-    }
-    if (taken) L.bitmap[w] = word | taken;
-    __syncthreads();
-    if (threadIdx.x == 1023) s_base = base + incl;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const int got = s_base < need ? s_base : need;
-    if (got < need) L.ctr[kCtrError] = 1;
-    L.ctr[kCtrFrames] = first_frame + nframes;
-    L.ctr[kCtrUsed] += got;
-  }
-}
-
-// Grid (nframes*ppf, H): copy one head's 64 slots of one frame page.  K rows
-// are copied as they are; V rows are transposed through LDS.  Slots past the
-// frame's last row are zero-filled.  T = uint16_t (bf16 bits) or float.
+// Grid (ppf, H): copy one head's 64 slots of one page of frame `frame` into
+// the page the host chose for it.  K rows are copied as they are; V rows are
+// transposed through LDS.  Slots past the frame's last row are zero-filled.
+// Workgroup (0, 0) records the pages in the frame table and the bitmap.
+// T = uint16_t (bf16 bits) or float.
 template <typename T>
 __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict__ kin,
-                                                const T* __restrict__ vin, int first_frame,
-                                                int ppf, int F, int H) {
+                                                const T* __restrict__ vin, int frame,
+                                                FramePages pages, int ppf, int F, int H) {
   constexpr int D = kHeadDim, P = kPage;
-  const int pg = blockIdx.x, h = blockIdx.y;
-  const int fl = pg / ppf, j = pg % ppf;
-  const int page = L.ftab[(first_frame + fl) * ppf + j];
-  if (page < 0) {
-    if (threadIdx.x == 0) L.ctr[kCtrError] = 2;
-    return;
-  }
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int page = pages.p[j];
   T* kdst = reinterpret_cast<T*>(L.kpool) + ((size_t)page * H + h) * P * D;
   T* vdst = reinterpret_cast<T*>(L.vpool) + ((size_t)page * H + h) * D * P;
   __shared__ T tile[P][D + 1];
-  const int row0 = fl * F + j * P;
+  const int row0 = j * P;
   const int nvalid = min(P, F - j * P);
   for (int e = threadIdx.x; e < P * D; e += 256) {
     const int s = e / D, d = e % D;
@@ -132,92 +77,16 @@ __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict_
     const int d = e / P, c = e % P;
     vdst[e] = tile[swap23(c)][d];
   }
-}
-
-// Lowest free page of the pool (block-wide), or -1.
-__device__ int block_lowest_free(const uint32_t* bitmap, int pool_pages, int* s_min) {
-  if (threadIdx.x == 0) *s_min = 0x7fffffff;
-  __syncthreads();
-  const int nwords = (pool_pages + 31) >> 5;
-  for (int w = threadIdx.x; w < nwords; w += blockDim.x) {
-    const int tail = pool_pages & 31;
-    const uint32_t valid = (w == nwords - 1 && tail) ? ((1u << tail) - 1u) : 0xffffffffu;
-    const uint32_t fb = ~bitmap[w] & valid;
-    if (fb) {
-      atomicMin(s_min, w * 32 + __ffs(fb) - 1);
-      break;  // later words of this thread hold larger pages
-    }
-  }
-  __syncthreads();
-  const int p = *s_min;
-  __syncthreads();
-  return p == 0x7fffffff ? -1 : p;
-}
-
-// One workgroup: move frame `frame`'s S summary rows to the trajectory memory
-// (new tail page first if needed), then free the frame's pages.
-template <typename T>
-__global__ __launch_bounds__(256) void k_evict(LayerDev L, int pool_pages, int frame, int ppf,
-                                               int S, int H) {
-  constexpr int D = kHeadDim, P = kPage;
-  __shared__ int s_min;
-  __shared__ int s_ctr[2];
-  if (threadIdx.x == 0) {
-    s_ctr[0] = L.ctr[kCtrTraj];
-    s_ctr[1] = L.ctr[kCtrSumPages];
-  }
-  __syncthreads();
-  const int traj = s_ctr[0];
-  const int nsp_old = s_ctr[1];
-  const int g0 = S * traj;
-  const int need = (g0 + S - 1) / P + 1 - nsp_old;  // 0 or 1 for S <= 64
-  int new_page = -1;
-  if (need > 0) {
-    new_page = block_lowest_free(L.bitmap, pool_pages, &s_min);
-    if (new_page < 0) {
-      if (threadIdx.x == 0) L.ctr[kCtrError] = 3;
-      return;
+  if (j == 0 && h == 0) {
+    if ((int)threadIdx.x < ppf) {
+      const int p = pages.p[threadIdx.x];
+      L.ftab[frame * ppf + threadIdx.x] = p;
+      atomicOr(&L.bitmap[p >> 5], 1u << (p & 31));
     }
     if (threadIdx.x == 0) {
-      L.bitmap[new_page >> 5] |= 1u << (new_page & 31);
-      L.slist[nsp_old] = new_page;
+      L.ctr[kCtrFrames] = frame + 1;
+      atomicAdd(&L.ctr[kCtrUsed], ppf);
     }
-  }
-  const int nsp = nsp_old + need;
-  T* kp = reinterpret_cast<T*>(L.kpool);
-  T* vp = reinterpret_cast<T*>(L.vpool);
-  if (need > 0) {  // a new summary page starts as zeros: its unused slots stay finite
-    const size_t base = (size_t)new_page * H * P * D;
-    for (int e = threadIdx.x; e < H * P * D; e += 256) {
-      kp[base + e] = T(0);
-      vp[base + e] = T(0);
-    }
-    __syncthreads();
-  }
-  if (L.ftab[frame * ppf] < 0) {  // the frame is not resident: corrupt state
-    if (threadIdx.x == 0) L.ctr[kCtrError] = 4;
-    return;
-  }
-  for (int e = threadIdx.x; e < S * H * D; e += 256) {
-    const int r = e / (H * D), h = (e / D) % H, d = e % D;
-    const int sp = L.ftab[frame * ppf + r / P], ss = r % P;
-    const int g = g0 + r;
-    const int dp = (g / P < nsp_old) ? L.slist[g / P] : new_page, ds = g % P;
-    kp[(((size_t)dp * H + h) * P + ds) * D + d] = kp[(((size_t)sp * H + h) * P + ss) * D + d];
-    vp[(((size_t)dp * H + h) * D + d) * P + swap23(ds)] =
-        vp[(((size_t)sp * H + h) * D + d) * P + swap23(ss)];
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < ppf) {
-    const int e = frame * ppf + threadIdx.x;
-    const int p = L.ftab[e];
-    if (p >= 0 && p < pool_pages) atomicAnd(&L.bitmap[p >> 5], ~(1u << (p & 31)));
-    L.ftab[e] = -1;
-  }
-  if (threadIdx.x == 0) {
-    L.ctr[kCtrTraj] = traj + 1;
-    L.ctr[kCtrSumPages] = nsp;
-    L.ctr[kCtrUsed] += need - ppf;
   }
 }
 
@@ -225,29 +94,34 @@ __global__ __launch_bounds__(256) void k_evict(LayerDev L, int pool_pages, int f
 // Attention over the page list
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid) {
+// Logical page i -> physical page and its valid slot count.  Fresh pages
+// (the frame being appended) report their index within the frame in `fj`
+// (else fj = -1).  A page index outside the pool (only possible if the page
+// table is corrupt) reads page 0 with every slot masked.
+__device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, int& fj) {
   const PageList& pl = a.pl;
+  fj = -1;
+  int pg;
   if (i < pl.a_cnt) {
     valid = (i % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-    return a.ftab[i];
-  }
-  i -= pl.a_cnt;
-  if (i < pl.s_cnt) {
+    pg = a.ftab[i];
+  } else if ((i -= pl.a_cnt) < pl.s_cnt) {
     valid = (i == pl.s_cnt - 1) ? pl.s_last_valid : kPage;
-    return a.slist[i];
+    pg = a.slist[i];
+  } else if ((i -= pl.s_cnt) < pl.w_cnt) {
+    const int e = pl.w_first + i;
+    valid = (e % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
+    pg = a.ftab[e];
+  } else {
+    i -= pl.w_cnt;
+    fj = i;
+    valid = (i == pl.ppf - 1) ? pl.f_last_valid : kPage;
+    pg = a.fresh.p[i];
   }
-  const int e = pl.w_first + (i - pl.s_cnt);
-  valid = (e % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-  return a.ftab[e];
-}
-
-// map_page with a range guard: a page index outside the pool (only possible
-// if the page table is corrupt) reads page 0 with every slot masked.
-__device__ __forceinline__ int map_page_safe(const AttnArgs& a, int i, int& valid) {
-  const int pg = map_page(a, i, valid);
   if ((unsigned)pg >= (unsigned)a.pool) {
     valid = 0;
-    return 0;
+    fj = -1;
+    pg = 0;
   }
   return pg;
 }
@@ -276,6 +150,20 @@ __device__ __forceinline__ void decode_wg(const AttnArgs& a, int& h, int& qb, in
   h = logical / (a.nsplit * a.qblocks);
 }
 
+// Bookkeeping of the appended frame, done once per launch.
+__device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
+  const int ppf = a.pl.ppf;
+  if ((int)threadIdx.x < ppf) {
+    const int p = a.fresh.p[threadIdx.x];
+    a.L.ftab[a.fresh_frame * ppf + threadIdx.x] = p;
+    atomicOr(&a.L.bitmap[p >> 5], 1u << (p & 31));
+  }
+  if (threadIdx.x == 0) {
+    a.L.ctr[kCtrFrames] = a.fresh_frame + 1;
+    atomicAdd(&a.L.ctr[kCtrUsed], ppf);
+  }
+}
+
 // bf16 attention, one workgroup = (head, 512 query rows, one key split).
 // 8 waves, wave w owns query rows [64w, 64w+64) of the block as two 32-row
 // tiles.  Per 64-key page, staged in LDS (double buffered):
@@ -288,6 +176,8 @@ __device__ __forceinline__ void decode_wg(const AttnArgs& a, int& h, int& qb, in
 // Operand layout of the 32x32x16 MFMA: A lane l holds row l%32, k 8(l/32)..+7;
 // B lane l holds column l%32, same k; accumulator register r of lane l is row
 // 8(r/4) + 4(l/32) + r%4, column l%32.
+// Pages of the frame being appended are read from k_in / v_in, staged like any
+// page, and written to their pool pages by the query-block-0 workgroups.
 __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
   constexpr int D = kHeadDim, P = kPage, LR = 72;  // LDS row: 64 bf16 + 8 pad
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][P * LR];
@@ -298,9 +188,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
   int h, qb, s;
   decode_wg(a, h, qb, s);
   const int H = a.H;
-  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt;
+  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = (int)((long long)npg * s / a.nsplit);
   const int p1 = (int)((long long)npg * (s + 1) / a.nsplit);
+  if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
 
   // Q^T fragments: tile j, d-chunk c: column q = 32j + l32, d = 16c + 8hf .. +7
   bf16x8 qf[2][4];
@@ -327,19 +218,51 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
   const float c2 = a.scale_log2;
 
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.kpool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.vpool);
+  uint16_t* kpool = reinterpret_cast<uint16_t*>(a.kpool);
+  uint16_t* vpool = reinterpret_cast<uint16_t*>(a.vpool);
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
+  const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
   const int ld_row = tid >> 3, ld_ch = tid & 7;  // 512 threads x 16 B = one 8 KB tile
 
-  int valid_cur = P;
+  // global -> registers for logical page i
+  auto load_page = [&](int i, uint4& kv, uint4& vv, int& valid, int& fj, size_t& off) {
+    const int pg = map_page(a, i, valid, fj);
+    off = ((size_t)pg * H + h) * (P * D);
+    if (fj < 0) {
+      kv = *reinterpret_cast<const uint4*>(kpool + off + tid * 8);
+      vv = *reinterpret_cast<const uint4*>(vpool + off + tid * 8);
+      if (valid < P) vv = mask_vt_chunk(vv, ld_ch, valid);
+    } else {
+      kv = make_uint4(0u, 0u, 0u, 0u);
+      vv = kv;
+      if (ld_row < valid) {
+        const size_t src = ((size_t)(fj * P + ld_row) * H + h) * D + ld_ch * 8;
+        kv = *reinterpret_cast<const uint4*>(kin + src);
+        vv = *reinterpret_cast<const uint4*>(vin + src);
+      }
+      if (qb == 0) *reinterpret_cast<uint4*>(kpool + off + tid * 8) = kv;
+    }
+  };
+  // registers -> LDS buffer b (V of a fresh page is transposed on the way)
+  auto store_page = [&](int b, const uint4& kv, const uint4& vv, int fj) {
+    *reinterpret_cast<uint4*>(&sK[b][ld_row * LR + ld_ch * 8]) = kv;
+    if (fj < 0) {
+      *reinterpret_cast<uint4*>(&sV[b][ld_row * LR + ld_ch * 8]) = vv;
+    } else {
+      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+      const int col = swap23(ld_row);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sV[b][(ld_ch * 8 + e) * LR + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    }
+  };
+
+  int valid_cur = P, fj_cur = -1;
+  size_t off_cur = 0;
   if (p0 < p1) {
-    const int pg = map_page_safe(a, p0, valid_cur);
-    const size_t off = ((size_t)pg * H + h) * (P * D);
-    const uint4 kv = *reinterpret_cast<const uint4*>(kpool + off + tid * 8);
-    uint4 vv = *reinterpret_cast<const uint4*>(vpool + off + tid * 8);
-    if (valid_cur < P) vv = mask_vt_chunk(vv, ld_ch, valid_cur);
-    *reinterpret_cast<uint4*>(&sK[0][ld_row * LR + ld_ch * 8]) = kv;
-    *reinterpret_cast<uint4*>(&sV[0][ld_row * LR + ld_ch * 8]) = vv;
+    uint4 kv, vv;
+    load_page(p0, kv, vv, valid_cur, fj_cur, off_cur);
+    store_page(0, kv, vv, fj_cur);
   }
   __syncthreads();
 
@@ -347,14 +270,14 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
     const int buf = (i - p0) & 1;
     // prefetch page i+1 into registers
     uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
-    int valid_next = P;
+    int valid_next = P, fj_next = -1;
+    size_t off_next = 0;
     const bool has_next = i + 1 < p1;
-    if (has_next) {
-      const int pg = map_page_safe(a, i + 1, valid_next);
-      const size_t off = ((size_t)pg * H + h) * (P * D);
-      kn = *reinterpret_cast<const uint4*>(kpool + off + tid * 8);
-      vn = *reinterpret_cast<const uint4*>(vpool + off + tid * 8);
-    }
+    if (has_next) load_page(i + 1, kn, vn, valid_next, fj_next, off_next);
+    // a fresh page just staged: its transposed V tile goes to the pool
+    if (fj_cur >= 0 && qb == 0)
+      *reinterpret_cast<uint4*>(vpool + off_cur + tid * 8) =
+          *reinterpret_cast<const uint4*>(&sV[buf][ld_row * LR + ld_ch * 8]);
 
     // S^T = K Q^T
     f32x16 sacc[2][2];
@@ -429,12 +352,10 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
       }
     }
 
-    if (has_next) {
-      if (valid_next < P) vn = mask_vt_chunk(vn, ld_ch, valid_next);
-      *reinterpret_cast<uint4*>(&sK[buf ^ 1][ld_row * LR + ld_ch * 8]) = kn;
-      *reinterpret_cast<uint4*>(&sV[buf ^ 1][ld_row * LR + ld_ch * 8]) = vn;
-    }
+    if (has_next) store_page(buf ^ 1, kn, vn, fj_next);
     valid_cur = valid_next;
+    fj_cur = fj_next;
+    off_cur = off_next;
     __syncthreads();
   }
 
@@ -480,8 +401,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
 
 // fp32 attention: one thread per query row (256-row blocks).  Each page is
 // staged in LDS; keys are taken one at a time with an online softmax.
-constexpr int kF32Rows = 256;
-
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   constexpr int D = kHeadDim, P = kPage;
   __shared__ float sK[P][D + 1];
@@ -489,9 +408,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   int h, qb, s;
   decode_wg(a, h, qb, s);
   const int H = a.H;
-  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt;
+  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = (int)((long long)npg * s / a.nsplit);
   const int p1 = (int)((long long)npg * (s + 1) / a.nsplit);
+  if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
   const int row = qb * kF32Rows + threadIdx.x;
   const bool live = row < a.Lq;
   const float* q = reinterpret_cast<const float*>(a.q);
@@ -503,18 +423,40 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const float c2 = a.scale_log2;
-  const float* kpool = reinterpret_cast<const float*>(a.kpool);
-  const float* vpool = reinterpret_cast<const float*>(a.vpool);
+  float* kpool = reinterpret_cast<float*>(a.kpool);
+  float* vpool = reinterpret_cast<float*>(a.vpool);
+  const float* kin = reinterpret_cast<const float*>(a.k_in);
+  const float* vin = reinterpret_cast<const float*>(a.v_in);
   for (int i = p0; i < p1; ++i) {
-    int valid;
-    const int pg = map_page_safe(a, i, valid);
+    int valid, fj;
+    const int pg = map_page(a, i, valid, fj);
     const size_t off = ((size_t)pg * H + h) * (P * D);
     __syncthreads();
-    for (int e = threadIdx.x; e < P * D; e += 256) {
-      sK[e / D][e % D] = kpool[off + e];
-      sV[e / P][e % P] = vpool[off + e];
+    if (fj < 0) {
+      for (int e = threadIdx.x; e < P * D; e += 256) {
+        sK[e / D][e % D] = kpool[off + e];
+        sV[e / P][e % P] = vpool[off + e];
+      }
+    } else {
+      for (int e = threadIdx.x; e < P * D; e += 256) {
+        const int r = e / D, d = e % D;
+        float kv = 0.f, vv = 0.f;
+        if (r < valid) {
+          const size_t src = ((size_t)(fj * P + r) * H + h) * D + d;
+          kv = kin[src];
+          vv = vin[src];
+        }
+        sK[r][d] = kv;
+        sV[d][swap23(r)] = vv;
+      }
     }
     __syncthreads();
+    if (fj >= 0 && qb == 0) {
+      for (int e = threadIdx.x; e < P * D; e += 256) {
+        kpool[off + e] = sK[e / D][e % D];
+        vpool[off + e] = sV[e / P][e % P];
+      }
+    }
 #pragma unroll 1
     for (int key = 0; key < valid; ++key) {
       float acc = 0.f;
@@ -549,33 +491,38 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   }
 }
 
-// Merge of the key splits: O = sum_s w_s O_s / sum_s w_s l_s with
-// w_s = exp2((m_s - max m) * scale * log2 e); LSE = scale * max m + ln(sum).
-// Block = 16 query rows x 16 four-float chunks of one head.
+// ---------------------------------------------------------------------------
+// Merge of the key splits + eviction, one launch
+// ---------------------------------------------------------------------------
+
+// Merge: O = sum_s w_s O_s / sum_s w_s l_s with w_s = exp2((m_s - max m) *
+// scale * log2 e); LSE = scale * max m + ln(sum).  Block = 16 query rows x 16
+// four-float chunks of one head.
 template <bool kF32>
-__global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
+__device__ void merge_block(const AttnArgs& a, int h, int rb) {
   constexpr int D = kHeadDim;
-  const int h = blockIdx.y;
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int row = rb * 16 + (threadIdx.x >> 4);
   const int d4 = (threadIdx.x & 15) * 4;
   if (row >= a.Lq) return;
   const int ns = a.nsplit;
   const float2* ml = a.part_ml + (size_t)h * ns * a.Lq_pad + row;
   float M = -INFINITY;
+#pragma unroll 4
   for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[(size_t)s * a.Lq_pad].x);
   const float c2 = a.scale_log2;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* po = a.part_o + ((size_t)h * ns * a.Lq_pad + row) * D + d4;
+#pragma unroll 4
   for (int s = 0; s < ns; ++s) {
     const float2 v = ml[(size_t)s * a.Lq_pad];
     const float w = exp2f((v.x - M) * c2);
     L = __builtin_fmaf(w, v.y, L);
-    const float4 po = *reinterpret_cast<const float4*>(
-        a.part_o + (((size_t)h * ns + s) * a.Lq_pad + row) * D + d4);
-    acc.x = __builtin_fmaf(w, po.x, acc.x);
-    acc.y = __builtin_fmaf(w, po.y, acc.y);
-    acc.z = __builtin_fmaf(w, po.z, acc.z);
-    acc.w = __builtin_fmaf(w, po.w, acc.w);
+    const float4 x = *reinterpret_cast<const float4*>(po + (size_t)s * a.Lq_pad * D);
+    acc.x = __builtin_fmaf(w, x.x, acc.x);
+    acc.y = __builtin_fmaf(w, x.y, acc.y);
+    acc.z = __builtin_fmaf(w, x.z, acc.z);
+    acc.w = __builtin_fmaf(w, x.w, acc.w);
   }
   const float inv = 1.f / L;
   const size_t o = ((size_t)row * a.H + h) * D + d4;
@@ -591,6 +538,67 @@ __global__ __launch_bounds__(256) void k_merge(AttnArgs a) {
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = w;
   }
   if (d4 == 0 && a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = M * a.scale + logf(L);
+}
+
+// Eviction, one workgroup per head: zero the head's slice of a new summary
+// page, copy the frame's S summary rows (K rows and V^T columns) into the
+// summary slots.  The head-0 workgroup also updates the page table: set the
+// new page, append it to the summary list, free the frame's pages.  Copies
+// read page contents only and the bookkeeping writes metadata only, so the
+// workgroups need no ordering among themselves.
+template <typename T>
+__device__ void evict_block(const LayerDev& L, const EvictPlan& e, int h, int H) {
+  constexpr int D = kHeadDim, P = kPage;
+  T* kp = reinterpret_cast<T*>(L.kpool);
+  T* vp = reinterpret_cast<T*>(L.vpool);
+  if (e.new_page >= 0) {
+    const size_t base = ((size_t)e.new_page * H + h) * P * D;
+    for (int x = threadIdx.x; x < P * D; x += blockDim.x) {
+      kp[base + x] = T(0);
+      vp[base + x] = T(0);
+    }
+    __syncthreads();
+  }
+  for (int x = threadIdx.x; x < e.S * D; x += blockDim.x) {
+    const int r = x / D, d = x % D;
+    const int sp = e.src.p[r / P], ss = r % P;
+    const int g = e.g0 + r;
+    const int dp = (g / P == e.tail_index) ? e.tail_page : e.new_page, ds = g % P;
+    kp[(((size_t)dp * H + h) * P + ds) * D + d] = kp[(((size_t)sp * H + h) * P + ss) * D + d];
+    vp[(((size_t)dp * H + h) * D + d) * P + swap23(ds)] =
+        vp[(((size_t)sp * H + h) * D + d) * P + swap23(ss)];
+  }
+  if (h == 0) {
+    if ((int)threadIdx.x < e.ppf) {
+      const int p = e.src.p[threadIdx.x];
+      atomicAnd(&L.bitmap[p >> 5], ~(1u << (p & 31)));
+      L.ftab[e.frame * e.ppf + threadIdx.x] = -1;
+    }
+    if (threadIdx.x == 0) {
+      int used = -e.ppf;
+      if (e.new_page >= 0) {
+        atomicOr(&L.bitmap[e.new_page >> 5], 1u << (e.new_page & 31));
+        L.slist[e.new_index] = e.new_page;
+        L.ctr[kCtrSumPages] = e.new_index + 1;
+        used += 1;
+      }
+      L.ctr[kCtrTraj] += 1;
+      atomicAdd(&L.ctr[kCtrUsed], used);
+    }
+  }
+}
+
+template <bool kF32>
+__global__ __launch_bounds__(256) void k_merge_evict(AttnArgs a, EvictPlan e, int merge_rowblocks,
+                                                     int merge_heads) {
+  const int b = blockIdx.x;
+  const int nmerge = merge_rowblocks * merge_heads;
+  if (b < nmerge) {
+    merge_block<kF32>(a, b / merge_rowblocks, b % merge_rowblocks);
+  } else {
+    using T = typename std::conditional<kF32, float, uint16_t>::type;
+    evict_block<T>(a.L, e, b - nmerge, a.H);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -609,22 +617,16 @@ hipError_t launch_reset(const LayerDev& L, int pool_words, int ftab_entries, int
   return hipGetLastError();
 }
 
-hipError_t launch_alloc_frames(const LayerDev& L, int pool_pages, int ppf, int first_frame,
-                               int nframes, hipStream_t st) {
-  hipLaunchKernelGGL(k_alloc_frames, dim3(1), dim3(1024), 0, st, L, pool_pages, ppf,
-                     first_frame, nframes);
-  return hipGetLastError();
-}
-
-hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int first_frame,
-                         int nframes, int ppf, int F, int H, bool f32, hipStream_t st) {
-  dim3 grid(nframes * ppf, H);
+hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int frame,
+                         const FramePages& pages, int ppf, int F, int H, bool f32,
+                         hipStream_t st) {
+  dim3 grid(ppf, H);
   if (f32)
     hipLaunchKernelGGL(k_append<float>, grid, dim3(256), 0, st, L, (const float*)k,
-                       (const float*)v, first_frame, ppf, F, H);
+                       (const float*)v, frame, pages, ppf, F, H);
   else
     hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(256), 0, st, L, (const uint16_t*)k,
-                       (const uint16_t*)v, first_frame, ppf, F, H);
+                       (const uint16_t*)v, frame, pages, ppf, F, H);
   return hipGetLastError();
 }
 
@@ -637,21 +639,18 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnArgs& a, bool f32, hipStream_t st) {
-  dim3 grid((a.Lq + 15) / 16, a.H);
+hipError_t launch_merge_evict(const AttnArgs& a, const EvictPlan* ev, bool f32, hipStream_t st) {
+  const int rowblocks = a.nsplit > 1 ? (a.Lq + 15) / 16 : 0;
+  const int mheads = a.nsplit > 1 ? a.H : 0;
+  const int eblocks = ev != nullptr ? a.H : 0;
+  const int grid = rowblocks * mheads + eblocks;
+  if (grid == 0) return hipSuccess;
+  EvictPlan e{};
+  if (ev != nullptr) e = *ev;
   if (f32)
-    hipLaunchKernelGGL(k_merge<true>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_merge_evict<true>, dim3(grid), dim3(256), 0, st, a, e, rowblocks, mheads);
   else
-    hipLaunchKernelGGL(k_merge<false>, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_evict(const LayerDev& L, int pool_pages, int frame, int ppf, int S, int H,
-                        bool f32, hipStream_t st) {
-  if (f32)
-    hipLaunchKernelGGL(k_evict<float>, dim3(1), dim3(256), 0, st, L, pool_pages, frame, ppf, S, H);
-  else
-    hipLaunchKernelGGL(k_evict<uint16_t>, dim3(1), dim3(256), 0, st, L, pool_pages, frame, ppf, S, H);
+    hipLaunchKernelGGL(k_merge_evict<false>, dim3(grid), dim3(256), 0, st, a, e, rowblocks, mheads);
   return hipGetLastError();
 }
 

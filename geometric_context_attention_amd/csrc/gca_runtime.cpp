@@ -80,6 +80,7 @@ int validate(const gca_config* c, std::string& why) {
   const int64_t F = (int64_t)c->image_tokens + c->summary_tokens;
   if ((int64_t)c->n_anchor * F > (1 << 24)) { why = "anchor block too large"; return GCA_E_INVALID_ARG; }
   const int64_t ppf = cdiv(F, kPage);
+  if (ppf > kMaxFramePages) { why = "frames of more than 2048 tokens are not supported"; return GCA_E_UNSUPPORTED; }
   if ((int64_t)c->max_frames * ppf > (1LL << 30)) { why = "max_frames too large"; return GCA_E_INVALID_ARG; }
   return GCA_OK;
 }
@@ -130,11 +131,50 @@ void make_geometry(const gca_config& c, Geometry& g) {
   g.scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
 }
 
+// Host mirror of one layer's page table.  The host takes every allocation
+// decision (lowest free page first) and passes the page ids to the kernels,
+// which write the device copy of the table; both copies evolve identically.
 struct LayerHost {
   bool streaming = false;
   int frames = 0;  // frames appended
   int traj = 0;    // frames in trajectory memory
   int used = 0;    // pages in use
+  int hint = 0;    // no page below this index is free
+  std::vector<uint32_t> bits;
+  std::vector<int32_t> ftab;
+  std::vector<int32_t> slist;
+
+  void init(const Geometry& g) {
+    streaming = false;
+    frames = traj = used = hint = 0;
+    bits.assign((size_t)g.words, 0u);
+    ftab.assign((size_t)g.ftab_entries, -1);
+    slist.assign((size_t)g.max_sum_pages, -1);
+  }
+  int alloc(int pool) {
+    int p = hint;
+    while (p < pool && (bits[p >> 5] >> (p & 31) & 1u)) ++p;
+    if (p >= pool) return -1;
+    bits[p >> 5] |= 1u << (p & 31);
+    hint = p + 1;
+    ++used;
+    return p;
+  }
+  void release(int p) {
+    bits[p >> 5] &= ~(1u << (p & 31));
+    if (p < hint) hint = p;
+    --used;
+  }
+  // Pages for frame f, lowest free first, in ascending order.
+  bool alloc_frame(int f, int ppf, int pool, FramePages& out) {
+    for (int j = 0; j < ppf; ++j) {
+      const int p = alloc(pool);
+      if (p < 0) return false;
+      out.p[j] = p;
+      ftab[(size_t)f * ppf + j] = p;
+    }
+    return true;
+  }
 };
 
 struct EventPair {
@@ -179,9 +219,12 @@ int harvest(gca_ctx* c, EventPair& e) {
   return GCA_OK;
 }
 
-// Launch attention (+ merge) over the page list `pl` for `Lq` query rows.
-int run_attention(gca_ctx* c, int layer, const void* q, void* out, float* lse, int Lq,
-                  const PageList& pl, int64_t keys, hipStream_t st) {
+// Attention over the page list `pl` for `Lq` query rows (appending the frame
+// `fresh_frame` from k/v when pl.fresh_cnt > 0), then the merge of the key
+// splits and the eviction `ev` (if any) in a second launch.
+int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const void* v,
+                     void* out, float* lse, int Lq, const PageList& pl, const FramePages& fresh,
+                     int fresh_frame, const EvictPlan* ev, int64_t keys, hipStream_t st) {
   const gca_config& cfg = c->cfg;
   AttnArgs a{};
   a.q = q;
@@ -190,10 +233,16 @@ int run_attention(gca_ctx* c, int layer, const void* q, void* out, float* lse, i
   a.ftab = c->dev[layer].ftab;
   a.slist = c->dev[layer].slist;
   a.pl = pl;
+  a.fresh = fresh;
+  a.k_in = k;
+  a.v_in = v;
+  a.fresh_frame = fresh_frame;
+  a.L = c->dev[layer];
   a.Lq = Lq;
   a.H = cfg.num_heads;
+  a.F = c->g.F;
   a.qblocks = (int)cdiv(Lq, query_rows(cfg));
-  const int64_t npg = (int64_t)pl.a_cnt + pl.s_cnt + pl.w_cnt;
+  const int64_t npg = (int64_t)pl.a_cnt + pl.s_cnt + pl.w_cnt + pl.fresh_cnt;
   a.nsplit = choose_splits(cfg, a.qblocks, npg);
   a.scale = c->g.scale;
   a.scale_log2 = (float)(c->g.scale * 1.4426950408889634);
@@ -221,10 +270,8 @@ int run_attention(gca_ctx* c, int layer, const void* q, void* out, float* lse, i
     ep->bytes = 2.0 * (double)keys * cfg.num_heads * cfg.head_dim * c->g.eb;
     ep->pending = true;
   }
-  if (a.nsplit > 1) {
-    e = launch_merge(a, c->f32, st);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
-  }
+  e = launch_merge_evict(a, ev, c->f32, st);
+  if (e != hipSuccess) return hip_fail(e, "merge/evict launch");
   return GCA_OK;
 }
 
@@ -301,7 +348,7 @@ int gca_reset(gca_ctx* c, void* stream) {
   for (int l = 0; l < c->cfg.num_layers; ++l) {
     hipError_t e = launch_reset(c->dev[l], c->g.words, (int)c->g.ftab_entries, c->g.max_sum_pages, st);
     if (e != hipSuccess) return hip_fail(e, "reset launch");
-    c->host[l] = LayerHost{};
+    c->host[l].init(c->g);
   }
   return GCA_OK;
 }
@@ -316,26 +363,28 @@ int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, con
   const gca_config& cfg = c->cfg;
   const Geometry& g = c->g;
   const int need = cfg.n_anchor * g.ppf;
-  if (need > g.pool) return fail(GCA_E_OUT_OF_PAGES, "pool cannot hold the anchor frames");
+  if (need > g.pool - hs.used) return fail(GCA_E_OUT_OF_PAGES, "pool cannot hold the anchor frames");
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_alloc_frames(c->dev[layer], g.pool, g.ppf, 0, cfg.n_anchor, st);
-  if (e != hipSuccess) return hip_fail(e, "alloc launch");
-  e = launch_append(c->dev[layer], k, v, 0, cfg.n_anchor, g.ppf, g.F, cfg.num_heads, c->f32, st);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  const size_t frame_bytes = (size_t)g.F * cfg.num_heads * cfg.head_dim * g.eb;
+  for (int f = 0; f < cfg.n_anchor; ++f) {
+    FramePages pages{};
+    hs.alloc_frame(f, g.ppf, g.pool, pages);
+    hipError_t e = launch_append(c->dev[layer], (const char*)k + f * frame_bytes,
+                                 (const char*)v + f * frame_bytes, f, pages, g.ppf, g.F,
+                                 cfg.num_heads, c->f32, st);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  }
   PageList pl{};
   pl.a_cnt = need;
-  pl.s_cnt = 0;
   pl.s_last_valid = kPage;
-  pl.w_first = 0;
-  pl.w_cnt = 0;
   pl.ppf = g.ppf;
   pl.f_last_valid = g.f_last_valid;
   const int Lq = cfg.n_anchor * g.F;
-  rc = run_attention(c, layer, q, out, lse, Lq, pl, (int64_t)Lq, st);
+  FramePages none{};
+  rc = run_step_kernels(c, layer, q, k, v, out, lse, Lq, pl, none, -1, nullptr, (int64_t)Lq, st);
   if (rc != GCA_OK) return rc;
   hs.streaming = true;
   hs.frames = cfg.n_anchor;
-  hs.used = need;
   hs.traj = 0;
   return GCA_OK;
 }
@@ -359,30 +408,46 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
   if ((int64_t)hs.used + g.ppf + new_sum > g.pool)
     return fail(GCA_E_OUT_OF_PAGES, "page pool exhausted at frame " + std::to_string(t));
   hipStream_t st = (hipStream_t)stream;
-  const LayerDev& d = c->dev[layer];
-  hipError_t e = launch_alloc_frames(d, g.pool, g.ppf, t, 1, st);
-  if (e != hipSuccess) return hip_fail(e, "alloc launch");
-  e = launch_append(d, k, v, t, 1, g.ppf, g.F, cfg.num_heads, c->f32, st);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
+  // pages of frame t (lowest free first); then, if frame t-k leaves the
+  // window, a new summary page (before its pages are freed)
+  FramePages fresh{};
+  hs.alloc_frame(t, g.ppf, g.pool, fresh);
+  EvictPlan ev{};
+  if (evict) {
+    const int fe = t - kw;
+    ev.frame = fe;
+    ev.ppf = g.ppf;
+    ev.S = S;
+    ev.g0 = S * hs.traj;
+    for (int j = 0; j < g.ppf; ++j) ev.src.p[j] = hs.ftab[(size_t)fe * g.ppf + j];
+    ev.tail_index = nsp - 1;
+    ev.tail_page = nsp > 0 ? hs.slist[nsp - 1] : -1;
+    ev.new_page = -1;
+    ev.new_index = nsp;
+    if (new_sum > 0) {
+      ev.new_page = hs.alloc(g.pool);
+      hs.slist[nsp] = ev.new_page;
+    }
+  }
   PageList pl{};
   pl.a_cnt = n * g.ppf;
   pl.s_cnt = nsp;
   pl.s_last_valid = nsp > 0 ? (int)((int64_t)S * hs.traj - (int64_t)(nsp - 1) * kPage) : kPage;
   pl.w_first = (t - w) * g.ppf;
-  pl.w_cnt = (w + 1) * g.ppf;
+  pl.w_cnt = w * g.ppf;
+  pl.fresh_cnt = g.ppf;
   pl.ppf = g.ppf;
   pl.f_last_valid = g.f_last_valid;
   const int64_t keys = (int64_t)(n + w + 1) * g.F + (int64_t)S * hs.traj;
-  rc = run_attention(c, layer, q, out, lse, g.F, pl, keys, st);
+  rc = run_step_kernels(c, layer, q, k, v, out, lse, g.F, pl, fresh, t, evict ? &ev : nullptr,
+                        keys, st);
   if (rc != GCA_OK) return rc;
-  if (evict) {
-    e = launch_evict(d, g.pool, t - kw, g.ppf, S, cfg.num_heads, c->f32, st);
-    if (e != hipSuccess) return hip_fail(e, "evict launch");
-  }
   hs.frames = t + 1;
-  hs.used += g.ppf;
   if (evict) {
-    hs.used += new_sum - g.ppf;
+    for (int j = 0; j < g.ppf; ++j) {
+      hs.release(ev.src.p[j]);
+      hs.ftab[(size_t)ev.frame * g.ppf + j] = -1;
+    }
     hs.traj += 1;
   }
   return GCA_OK;

@@ -168,12 +168,14 @@ def anchor_init(q, k, v, scale: float):
 def step(t: int, q_t, get_rows, shp: GcaShape, scale: float):
     """GCA output for streaming frame t >= n.
 
-    q_t: [F, H, D] queries of frame t.
-    get_rows(f, rows) -> (k_rows, v_rows), each [len(rows), H, D]: the key and
-    value rows of frame f at the given row indices.
+    q_t: [Lq, H', D] queries of frame t (all F rows, or any subset of rows;
+    H' may be a subset of the heads as long as get_rows returns the same).
+    get_rows(f, rows) -> (k_rows, v_rows), each [len(rows), H', D]: the key
+    and value rows of frame f at the given row indices.
 
     The per-step key mask over all (t+1)*F tokens is materialised and the
-    visible columns gathered frame by frame.
+    visible columns gathered frame by frame.  The result does not depend on
+    which query rows are passed (the rule does not depend on the query row).
     """
     if t < shp.n:
         raise ValueError("step() is for streaming frames t >= n")

@@ -48,12 +48,13 @@ def swap23(s):
     return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
 
 
-def check_state(stack: G.GcaStack, layer: int, pm: PageModel, rows_of=None):
+def check_state(stack: G.GcaStack, layer: int, pm: PageModel, rows_of=None, rows_of_batch=None):
     """Device page-table state equals the page model bit for bit; optionally
     the cached K/V bytes equal the input rows.
 
-    rows_of(f, rows) -> (k [len, H, D], v [len, H, D]) device tensors of the
-    input bits of frame f.
+    rows_of(f, rows) -> (k [len, H, D], v [len, H, D]) device tensors holding
+    the input bits of frame f; or rows_of_batch(frames, rows) -> (k, v)
+    [N, H, D] for arrays of (frame, row) pairs.
     """
     st = stack.export_state(layer)
     assert st["device_error"] == 0, f"device error flag {st['device_error']}"
@@ -73,22 +74,28 @@ def check_state(stack: G.GcaStack, layer: int, pm: PageModel, rows_of=None):
     ns = len(pm.summary_pages)
     assert sp[:ns].tolist() == pm.summary_pages
     assert (sp[ns:] == -1).all()
-    if rows_of is None:
+    if rows_of is None and rows_of_batch is None:
         return
     kpool, vpool = stack.pools(layer)
     loc = pm.resident_locations()
-    by_frame = {}
-    for (f, r), (p, s) in loc.items():
-        by_frame.setdefault(f, []).append((r, p, s))
+    items = sorted(loc.items())
+    fr = np.array([f for (f, _), _ in items])
+    rw = np.array([r for (_, r), _ in items])
+    pg = torch.tensor([p for _, (p, _) in items], device=kpool.device)
+    sl = np.array([s for _, (_, s) in items])
+    slots = torch.tensor(sl, device=kpool.device)
+    vcols = torch.tensor(swap23(sl), device=kpool.device)
+    if rows_of_batch is not None:
+        k_in, v_in = rows_of_batch(fr, rw)
+    else:
+        ks, vs = [], []
+        for f in np.unique(fr):
+            sel = fr == f
+            a, b = rows_of(int(f), rw[sel].tolist())
+            ks.append(a); vs.append(b)
+        k_in, v_in = torch.cat(ks), torch.cat(vs)
     iv = torch.int16 if stack.dtype == torch.bfloat16 else torch.int32
-    for f, lst in by_frame.items():
-        lst.sort()
-        rows = [r for r, _, _ in lst]
-        pages = torch.tensor([p for _, p, _ in lst], device=kpool.device)
-        slots = torch.tensor([s for _, _, s in lst], device=kpool.device)
-        vcols = torch.tensor(swap23(np.array([s for _, _, s in lst])), device=kpool.device)
-        k_in, v_in = rows_of(f, rows)
-        k_got = kpool[pages, :, slots, :]              # [N, H, D]
-        v_got = vpool[pages, :, :, vcols]              # [N, H, D]
-        assert torch.equal(k_got.view(iv), k_in.contiguous().view(iv)), f"K bytes of frame {f}"
-        assert torch.equal(v_got.view(iv), v_in.contiguous().view(iv)), f"V bytes of frame {f}"
+    k_got = kpool[pg, :, slots, :]              # [N, H, D]
+    v_got = vpool[pg, :, :, vcols]              # [N, H, D]
+    assert torch.equal(k_got.view(iv), k_in.to(kpool.device).contiguous().view(iv)), "cached K bytes differ"
+    assert torch.equal(v_got.view(iv), v_in.to(kpool.device).contiguous().view(iv)), "cached V bytes differ"
