@@ -165,8 +165,8 @@ __device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
 }
 
 // bf16 attention, one workgroup = (head, 512 query rows, one key split).
-// 8 waves, wave w owns query rows [64w, 64w+64) of the block as two 32-row
-// tiles.  Per 64-key page, staged in LDS (double buffered):
+// 8 waves; wave w owns query rows [64w, 64w+64) of the block as two 32-row
+// tiles j.  Keys are taken in 32-key tiles (two per 64-slot page):
 //   S^T[key][q] = K Q^T   v_mfma_f32_32x32x16_bf16, A = K (LDS), B = Q^T (regs)
 //   online softmax per query column, p = exp2((s - m) * scale * log2 e)
 //   O^T[d][q] += V^T P^T  A = V^T (LDS), B = P^T straight from the S^T
@@ -176,12 +176,176 @@ __device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
 // Operand layout of the 32x32x16 MFMA: A lane l holds row l%32, k 8(l/32)..+7;
 // B lane l holds column l%32, same k; accumulator register r of lane l is row
 // 8(r/4) + 4(l/32) + r%4, column l%32.
+//
+// Software pipeline: while the VALU computes the softmax of key tile u, the
+// MFMA pipe works on QK^T of tile u+1 and on PV of tile u-1; the three are
+// independent, so one wave keeps both units busy.  Pages are staged through
+// a triple LDS buffer (K runs one page ahead of V), one barrier per page.
+// The running max is only moved (and O rescaled) when it grows by more than
+// 2^8 in probability units, which keeps p <= 256 and the sums in fp32 range.
 // Pages of the frame being appended are read from k_in / v_in, staged like any
 // page, and written to their pool pages by the query-block-0 workgroups.
-__global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct PageInfo {
+  int valid;
+  int fj;       // index within the appended frame, or -1
+  size_t off;   // element offset of the head's slice in the pools
+};
+
+constexpr float kLazyRescaleLog2 = 8.0f;
+#ifndef GCA_ATTN_WAVES
+#define GCA_ATTN_WAVES 8
+#endif
+constexpr int kAttnWaves = GCA_ATTN_WAVES;  // 8 waves = 2 per SIMD
+
+template <int NJ>
+__device__ __forceinline__ void qk_tile(const uint16_t* sKb, int kt, const bf16x8 (&qf)[NJ][4],
+                                        f32x16 (&sc)[NJ], int l32, int hf) {
+  constexpr int LR = 72;
+  const f32x16 zero = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sKb[(kt * 32 + l32) * LR + c * 16 + hf * 8]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[j], 0, 0, 0);
+  }
+}
+
+template <int NJ>
+__device__ __forceinline__ void mask_tile(f32x16 (&sc)[NJ], int valid, int kt, int hf) {
+  if (valid >= kt * 32 + 32) return;  // wave-uniform
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    if (key >= valid) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) sc[j][r] = -INFINITY;
+    }
+  }
+}
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// max of a lane's value and the value of the lane 32 apart (the two halves of
+// a wave hold the two key halves of the same query column)
+__device__ __forceinline__ float half_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
+__device__ __forceinline__ float half_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
+                                                  __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Running max of tile sc; moves it (and rescales l and O) only when some
+// column's max grew by more than thr (raw score units).  O must already hold
+// every tile before this one.
+template <int NJ>
+__device__ __forceinline__ void softmax_max(const f32x16 (&sc)[NJ], float (&m)[NJ], float (&l)[NJ],
+                                            f32x16 (&o)[2][NJ], float c2, float thr) {
+  float mx[NJ];
+  bool need = false;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const f32x16& v = sc[j];
+    const float a = max3f(v[0], v[1], v[2]), b = max3f(v[3], v[4], v[5]);
+    const float c = max3f(v[6], v[7], v[8]), d = max3f(v[9], v[10], v[11]);
+    const float e = max3f(v[12], v[13], v[14]);
+    mx[j] = half_pair_max(fmaxf(max3f(a, b, c), max3f(d, e, v[15])));
+    need |= mx[j] - m[j] > thr;
+  }
+  if (__any(need)) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float mnew = fmaxf(m[j], mx[j]);
+      const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * c2);
+      l[j] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        o[0][j][r] *= alpha;
+        o[1][j][r] *= alpha;
+      }
+      m[j] = mnew;
+    }
+  }
+}
+
+// p = exp2((s - m) * scale * log2 e) as packed bf16 P^T fragments; the row
+// sums accumulate the same rounded values (v_dot2 with (1, 1)).
+template <int NJ>
+__device__ __forceinline__ void softmax_exp(const f32x16 (&sc)[NJ], const float (&m)[NJ],
+                                            float (&l)[NJ], bf16x8 (&pf)[NJ][2], float c2) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const float mc = m[j] * c2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      pf[j][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][r], c2, -mc));
+    float acc = l[j];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pf[j][hh][e], pf[j][hh][e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+      }
+    l[j] = acc;
+  }
+  // Keep the exponentials in this block, next to the MFMAs they overlap
+  // with, instead of letting the compiler sink them towards their use in the
+  // next page step (an empty statement that only reads the fragments).
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) asm volatile("" ::"v"(pf[j][hh]));
+}
+
+// Scheduling hint for a block holding 8 QK^T MFMAs and the softmax VALU work
+// of one tile: alternate one MFMA with a run of VALU instructions.
+__device__ __forceinline__ void interleave_hint() {
+#ifdef GCA_SCHED_HINTS
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, GCA_SCHED_HINTS, 0);
+  }
+#endif
+}
+
+template <int NJ>
+__device__ __forceinline__ void pv_tile(const uint16_t* sVb, int kt, const bf16x8 (&pf)[NJ][2],
+                                        f32x16 (&o)[2][NJ], int l32, int hf) {
+  constexpr int LR = 72;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int kc = kt * 2 + hh;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sVb[(dt * 32 + l32) * LR + kc * 16 + hf * 8]);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][hh], o[dt][j], 0, 0, 0);
+    }
+  }
+}
+
+// NW waves of 64 lanes; wave w owns query rows [w*32*NJ, (w+1)*32*NJ) of the
+// 512-row block as NJ tiles of 32 rows (NW * NJ = 16).
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
+  constexpr int NJ = 16 / NW;
+  constexpr int NT = NW * 64;          // threads
+  constexpr int CPT = 512 / NT;        // 16-byte chunks of an 8 KB tile per thread
   constexpr int D = kHeadDim, P = kPage, LR = 72;  // LDS row: 64 bf16 + 8 pad
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][P * LR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * LR];
+  constexpr int TILE = P * LR;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -194,11 +358,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
   if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
 
   // Q^T fragments: tile j, d-chunk c: column q = 32j + l32, d = 16c + 8hf .. +7
-  bf16x8 qf[2][4];
+  bf16x8 qf[NJ][4];
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
+  for (int j = 0; j < NJ; ++j) {
+    const int row = qb * kQBlock + wave * 32 * NJ + j * 32 + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -208,164 +372,187 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
     }
   }
 
-  f32x16 o[2][2];
+  f32x16 o[2][NJ];
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  float m[NJ], l[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+  }
   const float c2 = a.scale_log2;
+  const float thr = kLazyRescaleLog2 / c2;  // in raw score units
 
   uint16_t* kpool = reinterpret_cast<uint16_t*>(a.kpool);
   uint16_t* vpool = reinterpret_cast<uint16_t*>(a.vpool);
   const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
   const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
-  const int ld_row = tid >> 3, ld_ch = tid & 7;  // 512 threads x 16 B = one 8 KB tile
 
-  // global -> registers for logical page i
-  auto load_page = [&](int i, uint4& kv, uint4& vv, int& valid, int& fj, size_t& off) {
-    const int pg = map_page(a, i, valid, fj);
-    off = ((size_t)pg * H + h) * (P * D);
-    if (fj < 0) {
-      kv = *reinterpret_cast<const uint4*>(kpool + off + tid * 8);
-      vv = *reinterpret_cast<const uint4*>(vpool + off + tid * 8);
-      if (valid < P) vv = mask_vt_chunk(vv, ld_ch, valid);
-    } else {
-      kv = make_uint4(0u, 0u, 0u, 0u);
-      vv = kv;
-      if (ld_row < valid) {
-        const size_t src = ((size_t)(fj * P + ld_row) * H + h) * D + ld_ch * 8;
-        kv = *reinterpret_cast<const uint4*>(kin + src);
-        vv = *reinterpret_cast<const uint4*>(vin + src);
-      }
-      if (qb == 0) *reinterpret_cast<uint4*>(kpool + off + tid * 8) = kv;
-    }
+  auto info_of = [&](int i) {
+    PageInfo pi;
+    const int pg = map_page(a, i, pi.valid, pi.fj);
+    pi.off = ((size_t)pg * H + h) * (P * D);
+    return pi;
   };
-  // registers -> LDS buffer b (V of a fresh page is transposed on the way)
-  auto store_page = [&](int b, const uint4& kv, const uint4& vv, int fj) {
-    *reinterpret_cast<uint4*>(&sK[b][ld_row * LR + ld_ch * 8]) = kv;
-    if (fj < 0) {
-      *reinterpret_cast<uint4*>(&sV[b][ld_row * LR + ld_ch * 8]) = vv;
-    } else {
-      const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-      const int col = swap23(ld_row);
+  // chunk x of a tile = 16 bytes at element 8x: row x/8, column chunk x%8
+  auto load_k = [&](const PageInfo& pi, uint4 (&kv)[CPT]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sV[b][(ld_ch * 8 + e) * LR + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    for (int u = 0; u < CPT; ++u) {
+      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
+      if (pi.fj < 0) {
+        kv[u] = *reinterpret_cast<const uint4*>(kpool + pi.off + x * 8);
+      } else {
+        kv[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (row < pi.valid)
+          kv[u] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pi.fj * P + row) * H + h) * D + ch * 8);
+        if (qb == 0) *reinterpret_cast<uint4*>(kpool + pi.off + x * 8) = kv[u];
+      }
+    }
+  };
+  auto load_v = [&](const PageInfo& pi, uint4 (&vv)[CPT]) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
+      vv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (pi.fj < 0) {
+        vv[u] = *reinterpret_cast<const uint4*>(vpool + pi.off + x * 8);
+        if (pi.valid < P) vv[u] = mask_vt_chunk(vv[u], ch, pi.valid);
+      } else if (row < pi.valid) {
+        vv[u] = *reinterpret_cast<const uint4*>(vin + ((size_t)(pi.fj * P + row) * H + h) * D + ch * 8);
+      }
+    }
+  };
+  auto store_k = [&](int b, const uint4 (&kv)[CPT]) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int x = tid + u * NT;
+      *reinterpret_cast<uint4*>(&sK[b][(x >> 3) * LR + (x & 7) * 8]) = kv[u];
+    }
+  };
+  auto store_v = [&](int b, const uint4 (&vv)[CPT], int fj) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
+      if (fj < 0) {
+        *reinterpret_cast<uint4*>(&sV[b][row * LR + ch * 8]) = vv[u];
+      } else {  // rows of the input: transpose into V^T on the way
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        const int col = swap23(row);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sV[b][(ch * 8 + e) * LR + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+      }
     }
   };
 
-  int valid_cur = P, fj_cur = -1;
-  size_t off_cur = 0;
-  if (p0 < p1) {
-    uint4 kv, vv;
-    load_page(p0, kv, vv, valid_cur, fj_cur, off_cur);
-    store_page(0, kv, vv, fj_cur);
+  // prologue: K and V of page p0, K of page p0+1; the V buffer of "page
+  // p0-1" is zeroed so that the first PV of the loop (with P = 0) is a no-op
+  PageInfo pi0 = info_of(p0);
+  PageInfo pi1{P, -1, 0}, pi2{P, -1, 0};
+  {
+    uint4 kv[CPT], vv[CPT];
+    load_k(pi0, kv);
+    load_v(pi0, vv);
+    store_k(0, kv);
+    store_v(0, vv, pi0.fj);
+    if (p0 + 1 < p1) {
+      pi1 = info_of(p0 + 1);
+      load_k(pi1, kv);
+      store_k(1, kv);
+    }
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int x = tid + u * NT;
+      *reinterpret_cast<uint4*>(&sV[2][(x >> 3) * LR + (x & 7) * 8]) = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   __syncthreads();
 
-  for (int i = p0; i < p1; ++i) {
-    const int buf = (i - p0) & 1;
-    // prefetch page i+1 into registers
-    uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
-    int valid_next = P, fj_next = -1;
-    size_t off_next = 0;
-    const bool has_next = i + 1 < p1;
-    if (has_next) load_page(i + 1, kn, vn, valid_next, fj_next, off_next);
-    // a fresh page just staged: its transposed V tile goes to the pool
-    if (fj_cur >= 0 && qb == 0)
-      *reinterpret_cast<uint4*>(vpool + off_cur + tid * 8) =
-          *reinterpret_cast<const uint4*>(&sV[buf][ld_row * LR + ld_ch * 8]);
+  f32x16 s_cur[NJ], s_nxt[NJ];
+  bf16x8 p_cur[NJ][2], p_prev[NJ][2];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p_prev[j][hh][e] = (__bf16)0.0f;
+  qk_tile<NJ>(sK[0], 0, qf, s_cur, l32, hf);
 
-    // S^T = K Q^T
-    f32x16 sacc[2][2];
+  int b0 = 0, b1 = 1, b2 = 2;  // buffers of pages i, i+1, i+2 (V of page i-1 is in b2)
+  // One page: tiles u = (i, 0) and (i, 1).  Each half: mask the tile whose
+  // QK^T was issued in the previous half, issue PV of the previous tile, move
+  // the running max, then one branch-free block with QK^T of the next tile on
+  // the MFMA pipe and the exponentials of this tile on the VALU.
+  auto page_step = [&](int i, auto has1_c, auto has2_c, auto masked_c) {
+    constexpr bool has1 = decltype(has1_c)::value, has2 = decltype(has2_c)::value;
+    constexpr bool masked = decltype(masked_c)::value;  // page i has empty slots
+    uint4 kn[CPT], vn[CPT];
+    if (has2) {
+      pi2 = info_of(i + 2);
+      load_k(pi2, kn);
+    }
+    if (has1) load_v(pi1, vn);
+    if (pi0.fj >= 0 && qb == 0) {  // the appended frame's V^T tile goes to its pool page
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][j][r] = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[buf][(kt * 32 + l32) * LR + c * 16 + hf * 8]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          sacc[kt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], sacc[kt][j], 0, 0, 0);
+      for (int u = 0; u < CPT; ++u) {
+        const int x = tid + u * NT;
+        *reinterpret_cast<uint4*>(vpool + pi0.off + x * 8) =
+            *reinterpret_cast<const uint4*>(&sV[b0][(x >> 3) * LR + (x & 7) * 8]);
       }
     }
-    if (valid_cur < P) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (key >= valid_cur) {
-            sacc[kt][0][r] = -INFINITY;
-            sacc[kt][1][r] = -INFINITY;
-          }
-        }
-    }
+    // half 0: tile (i, 0)
+    if (masked) mask_tile<NJ>(s_cur, pi0.valid, 0, hf);
+    pv_tile<NJ>(sV[b2], 1, p_prev, o, l32, hf);
+    softmax_max<NJ>(s_cur, m, l, o, c2, thr);
+    qk_tile<NJ>(sK[b0], 1, qf, s_nxt, l32, hf);
+    softmax_exp<NJ>(s_cur, m, l, p_cur, c2);
+    interleave_hint();
+    // half 1: tile (i, 1)
+    if (masked) mask_tile<NJ>(s_nxt, pi0.valid, 1, hf);
+    pv_tile<NJ>(sV[b0], 0, p_cur, o, l32, hf);
+    softmax_max<NJ>(s_nxt, m, l, o, c2, thr);
+    if (has1) qk_tile<NJ>(sK[b1], 0, qf, s_cur, l32, hf);
+    softmax_exp<NJ>(s_nxt, m, l, p_prev, c2);
+    interleave_hint();
 
-    // online softmax, one query column per lane and tile
-    bf16x8 pf[2][4];  // [j][16-key chunk]
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float mx = sacc[0][j][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][j][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[j], mx);
-      const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * c2);
-      const float mc = mnew * c2;
-      float sum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][j][r], c2, -mc));
-          sum += p;
-          pf[j][kt * 2 + (r >> 3)][r & 7] = (__bf16)p;
-        }
-      l[j] = l[j] * alpha + sum;
-      m[j] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][j][r] *= alpha;
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sV[buf][(dt * 32 + l32) * LR + kc * 16 + hf * 8]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kc], o[dt][j], 0, 0, 0);
-      }
-    }
-
-    if (has_next) store_page(buf ^ 1, kn, vn, fj_next);
-    valid_cur = valid_next;
-    fj_cur = fj_next;
-    off_cur = off_next;
+    if (has2) store_k(b2, kn);
+    if (has1) store_v(b1, vn, pi1.fj);
+    pi0 = pi1;
+    pi1 = pi2;
+    const int t0 = b0;
+    b0 = b1;
+    b1 = b2;
+    b2 = t0;
     __syncthreads();
+  };
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  // full pages take a body without any masking code (no branch splits the
+  // MFMA/VALU block); the few partial pages (a frame's last page, the
+  // summary tail) take the masked body
+  int i = p0;
+  for (; i + 2 < p1; ++i) {
+    if (pi0.valid == P)
+      page_step(i, T_{}, T_{}, F_{});
+    else
+      page_step(i, T_{}, T_{}, T_{});
   }
+  if (i + 1 < p1) page_step(i++, T_{}, F_{}, T_{});
+  page_step(i, F_{}, F_{}, T_{});
+  pv_tile<NJ>(sV[b2], 1, p_prev, o, l32, hf);  // tile (p1-1, 1)
 
   // epilogue
 #pragma unroll
-  for (int j = 0; j < 2; ++j) l[j] += __shfl_xor(l[j], 32);
+  for (int j = 0; j < NJ; ++j) l[j] = half_pair_sum(l[j]);
   const bool final_out = a.nsplit == 1;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
+  for (int j = 0; j < NJ; ++j) {
+    const int row = qb * kQBlock + wave * 32 * NJ + j * 32 + l32;
     if (final_out) {
       if (row < a.Lq) {
         const float inv = 1.f / l[j];
@@ -375,11 +562,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const int d = dt * 32 + 8 * g + 4 * hf;
-            __bf16 b0 = (__bf16)(o[dt][j][4 * g + 0] * inv), b1 = (__bf16)(o[dt][j][4 * g + 1] * inv);
-            __bf16 b2 = (__bf16)(o[dt][j][4 * g + 2] * inv), b3 = (__bf16)(o[dt][j][4 * g + 3] * inv);
+            __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
+            __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
             uint2 w;
-            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
             *reinterpret_cast<uint2*>(out + d) = w;
           }
         if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * a.scale + logf(l[j]);
@@ -635,7 +822,7 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, dim3(grid), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16, dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, dim3(grid), dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -456,8 +456,8 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
 void gca_destroy(gca_ctx* c) {
   if (c == nullptr) return;
   for (EventPair& e : c->ev) {
-    if (e.a) hipEventDestroy(e.a);
-    if (e.b) hipEventDestroy(e.b);
+    if (e.a) (void)hipEventDestroy(e.a);
+    if (e.b) (void)hipEventDestroy(e.b);
   }
   delete c;
 }
