@@ -48,7 +48,23 @@ def parse():
     ap.add_argument("--pool", type=int, default=64, help="resident input frames per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (x4) for counter calibration")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain elementwise copy of known size (fp32 x*1): each launch reads
+    and writes exactly mib MiB; used to scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 4,
+                      "copy_calibration_bytes_written_per_launch": n * 4, "launches": 4}))
 
 
 def log(msg):
@@ -63,8 +79,13 @@ def main():
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import torch
     from geometric_context_attention_amd import _lib as G
+    from geometric_context_attention_amd.profiling import read_traffic
     from geometric_context_attention_amd.synth import StreamSpec, draw_frames
 
     if not torch.cuda.is_available():
@@ -170,7 +191,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": read_traffic() if (T, Ly, k, M) == (10000, 12, 64, 500) else None,
             "avg_launch_us": round(attn_avg_ms * 1e3, 2),
             "launches": prof["attn_launches"],
             "algorithmic_flop_per_launch": prof["attn_flop"] / max(prof["attn_launches"], 1),
