@@ -98,20 +98,26 @@ __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict_
 // (the frame being appended) report their index within the frame in `fj`
 // (else fj = -1).  A page index outside the pool (only possible if the page
 // table is corrupt) reads page 0 with every slot masked.
+// The frame table and summary list are read through the constant address
+// space (scalar loads): the entries read here are never written during the
+// launch (the appended frame's pages come in the arguments), and scalar loads
+// do not count against the vector-memory counter the LDS copies are waited on.
+typedef const int32_t __attribute__((address_space(4)))* const_i32p;
+
 __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, int& fj) {
   const PageList& pl = a.pl;
   fj = -1;
   int pg;
   if (i < pl.a_cnt) {
     valid = (i % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-    pg = a.ftab[i];
+    pg = ((const_i32p)a.ftab)[i];
   } else if ((i -= pl.a_cnt) < pl.s_cnt) {
     valid = (i == pl.s_cnt - 1) ? pl.s_last_valid : kPage;
-    pg = a.slist[i];
+    pg = ((const_i32p)a.slist)[i];
   } else if ((i -= pl.s_cnt) < pl.w_cnt) {
     const int e = pl.w_first + i;
     valid = (e % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-    pg = a.ftab[e];
+    pg = ((const_i32p)a.ftab)[e];
   } else {
     i -= pl.w_cnt;
     fj = i;
@@ -126,16 +132,21 @@ __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, in
   return pg;
 }
 
-// Zero the V^T entries of slots >= valid in a 16-byte chunk of one d row
-// (stored columns 8*ch .. 8*ch+7), so that a masked key (probability 0) never
-// meets a non-finite value in the PV product.
-__device__ __forceinline__ uint4 mask_vt_chunk(uint4 v, int ch, int valid) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (swap23(ch * 8 + e) >= valid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+// Physical page of logical page i (loads through the constant space).
+__device__ __forceinline__ int page_id(const AttnArgs& a, int i) {
+  int valid, fj;
+  return map_page(a, i, valid, fj);
+}
+
+// Valid slots of logical page i (arithmetic only).
+__device__ __forceinline__ int page_valid(const AttnArgs& a, int i) {
+  const PageList& pl = a.pl;
+  if (i < pl.a_cnt) return (i % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
+  i -= pl.a_cnt;
+  if (i < pl.s_cnt) return (i == pl.s_cnt - 1) ? pl.s_last_valid : kPage;
+  i -= pl.s_cnt;
+  if (i < pl.w_cnt) return ((pl.w_first + i) % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
+  return (i - pl.w_cnt == pl.ppf - 1) ? pl.f_last_valid : kPage;
 }
 
 // Workgroup index -> (head, query block, split).  Workgroups are dealt to the
@@ -166,7 +177,7 @@ __device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
 
 // bf16 attention, one workgroup = (head, 512 query rows, one key split).
 // 8 waves; wave w owns query rows [64w, 64w+64) of the block as two 32-row
-// tiles j.  Keys are taken in 32-key tiles (two per 64-slot page):
+// tiles j.  Per 64-slot page:
 //   S^T[key][q] = K Q^T   v_mfma_f32_32x32x16_bf16, A = K (LDS), B = Q^T (regs)
 //   online softmax per query column, p = exp2((s - m) * scale * log2 e)
 //   O^T[d][q] += V^T P^T  A = V^T (LDS), B = P^T straight from the S^T
@@ -177,59 +188,34 @@ __device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
 // B lane l holds column l%32, same k; accumulator register r of lane l is row
 // 8(r/4) + 4(l/32) + r%4, column l%32.
 //
-// Software pipeline: while the VALU computes the softmax of key tile u, the
-// MFMA pipe works on QK^T of tile u+1 and on PV of tile u-1; the three are
-// independent, so one wave keeps both units busy.  Pages are staged through
-// a triple LDS buffer (K runs one page ahead of V), one barrier per page.
-// The running max is only moved (and O rescaled) when it grows by more than
-// 2^8 in probability units, which keeps p <= 256 and the sums in fp32 range.
-// Pages of the frame being appended are read from k_in / v_in, staged like any
-// page, and written to their pool pages by the query-block-0 workgroups.
+// Staging: pages go from HBM straight into a ring of four LDS slots with
+// global_load_lds_dwordx4 (no registers), three pages ahead of the one being
+// computed, which hides the HBM latency.  Each 8 KB tile (K [64][64] or V^T
+// [64][64]) is stored unpadded with an XOR swizzle: 16-byte chunk c of row r
+// sits at chunk c ^ ((r >> 1) & 7), so the fragment reads are bank-conflict free.
+// The loop is unrolled over the ring so every slot index is a constant (the
+// compiler can then tell the slots apart and only waits where this code asks
+// it to: vmcnt for the copies, one barrier per page).
+// The running max is only raised (and O rescaled) when a page's probabilities
+// against the current max grow too large (see valu_phase).
+// Pages of the frame being appended are first written to their pool pages by
+// the workgroups whose split holds them (V transposed through LDS), then read
+// back through the ring like any other page.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-struct PageInfo {
-  int valid;
-  int fj;       // index within the appended frame, or -1
-  size_t off;   // element offset of the head's slice in the pools
-};
-
-constexpr float kLazyRescaleLog2 = 8.0f;
-#ifndef GCA_ATTN_WAVES
-#define GCA_ATTN_WAVES 8
+#ifndef GCA_PINGPONG
+#define GCA_PINGPONG 1
 #endif
-constexpr int kAttnWaves = GCA_ATTN_WAVES;  // 8 waves = 2 per SIMD
-
-template <int NJ>
-__device__ __forceinline__ void qk_tile(const uint16_t* sKb, int kt, const bf16x8 (&qf)[NJ][4],
-                                        f32x16 (&sc)[NJ], int l32, int hf) {
-  constexpr int LR = 72;
-  const f32x16 zero = {};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sKb[(kt * 32 + l32) * LR + c * 16 + hf * 8]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[j], 0, 0, 0);
-  }
-}
-
-template <int NJ>
-__device__ __forceinline__ void mask_tile(f32x16 (&sc)[NJ], int valid, int kt, int hf) {
-  if (valid >= kt * 32 + 32) return;  // wave-uniform
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-    if (key >= valid) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) sc[j][r] = -INFINITY;
-    }
-  }
-}
+constexpr int kRing = 6;       // LDS page slots
+constexpr int kAhead = 4;      // a wave stages page j + kAhead while it computes page j
+static_assert(kRing >= kAhead + 2, "a slot is refilled only after both wave groups have read it");
+constexpr int kTileElems = 4096;
+constexpr int kAttnWaves = 8;  // 512 threads, 2 waves per SIMD
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// max of a lane's value and the value of the lane 32 apart (the two halves of
-// a wave hold the two key halves of the same query column)
+// max / sum of a lane's value and the value of the lane 32 apart (the two
+// halves of a wave hold the two key halves of the same query column)
 __device__ __forceinline__ float half_pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x),
                                                   __builtin_bit_cast(unsigned, x), false, false);
@@ -242,112 +228,250 @@ __device__ __forceinline__ float half_pair_sum(float x) {
   return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
-// Running max of tile sc; moves it (and rescales l and O) only when some
-// column's max grew by more than thr (raw score units).  O must already hold
-// every tile before this one.
-template <int NJ>
-__device__ __forceinline__ void softmax_max(const f32x16 (&sc)[NJ], float (&m)[NJ], float (&l)[NJ],
-                                            f32x16 (&o)[2][NJ], float c2, float thr) {
-  float mx[NJ];
-  bool need = false;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const f32x16& v = sc[j];
-    const float a = max3f(v[0], v[1], v[2]), b = max3f(v[3], v[4], v[5]);
-    const float c = max3f(v[6], v[7], v[8]), d = max3f(v[9], v[10], v[11]);
-    const float e = max3f(v[12], v[13], v[14]);
-    mx[j] = half_pair_max(fmaxf(max3f(a, b, c), max3f(d, e, v[15])));
-    need |= mx[j] - m[j] > thr;
-  }
-  if (__any(need)) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const float mnew = fmaxf(m[j], mx[j]);
-      const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * c2);
-      l[j] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        o[0][j][r] *= alpha;
-        o[1][j][r] *= alpha;
-      }
-      m[j] = mnew;
-    }
-  }
+// element offset of 16-byte chunk c of row r in a swizzled 64x64 tile: the
+// chunk index is XORed with (r >> 1) & 7, so the 16 rows one ds_read_b128
+// pass touches (two 128-byte rows per 256 bytes of banks) hit 16 different
+// 16-byte bank groups
+__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding; expcnt and
+// lgkmcnt left at their maxima)
+#define GCA_WAIT_VMCNT(N) __builtin_amdgcn_s_waitcnt(0x0F70 | ((N) & 15) | (((N) >> 4) << 14))
+
+// Workgroup barrier without a memory fence: the copies into LDS are made
+// visible by the explicit vmcnt wait before it, and the compiler is kept from
+// moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-// p = exp2((s - m) * scale * log2 e) as packed bf16 P^T fragments; the row
-// sums accumulate the same rounded values (v_dot2 with (1, 1)).
 template <int NJ>
-__device__ __forceinline__ void softmax_exp(const f32x16 (&sc)[NJ], const float (&m)[NJ],
-                                            float (&l)[NJ], bf16x8 (&pf)[NJ][2], float c2) {
+__device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (key >= valid) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sc[kt][j][r] = -INFINITY;
+      }
+    }
+}
+
+// p = exp2((s - m) * scale * log2 e) as packed bf16 P^T fragments
+// (pf[j][kc]: 16-key chunk kc of the page); psum[j] is the sum of the same
+// rounded values over this lane's 32 keys (v_dot2 with (1, 1)).
+template <int NJ>
+__device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float (&m)[NJ],
+                                         bf16x8 (&pf)[NJ][4], float (&psum)[NJ], float c2) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const float mc = m[j] * c2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      pf[j][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[j][r], c2, -mc));
-    float acc = l[j];
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int r = 0; r < 16; ++r)
+        pf[j][kt * 2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][j][r], c2, -mc));
+    float acc = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pf[j][hh][e], pf[j][hh][e + 1]};
+        const bf16x2 pr = {pf[j][kc][e], pf[j][kc][e + 1]};
         acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
       }
-    l[j] = acc;
+    psum[j] = acc;
   }
-  // Keep the exponentials in this block, next to the MFMAs they overlap
-  // with, instead of letting the compiler sink them towards their use in the
-  // next page step (an empty statement that only reads the fragments).
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) asm volatile("" ::"v"(pf[j][hh]));
 }
 
-// Scheduling hint for a block holding 8 QK^T MFMAs and the softmax VALU work
-// of one tile: alternate one MFMA with a run of VALU instructions.
-__device__ __forceinline__ void interleave_hint() {
-#ifdef GCA_SCHED_HINTS
+// Move the running max to the page's column max where that is larger and
+// rescale l and O by the drop in exp2 units.
+template <int NJ>
+__device__ __forceinline__ void raise_max(const f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
+                                          f32x16 (&o)[2][NJ], float c2) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, GCA_SCHED_HINTS, 0);
+  for (int j = 0; j < NJ; ++j) {
+    const f32x16& u = sc[0][j];
+    const f32x16& v = sc[1][j];
+    const float a = max3f(u[0], u[1], u[2]), b = max3f(u[3], u[4], u[5]);
+    const float c = max3f(u[6], u[7], u[8]), d = max3f(u[9], u[10], u[11]);
+    const float e = max3f(u[12], u[13], u[14]), f = max3f(u[15], v[0], v[1]);
+    const float g = max3f(v[2], v[3], v[4]), h = max3f(v[5], v[6], v[7]);
+    const float i = max3f(v[8], v[9], v[10]), k = max3f(v[11], v[12], v[13]);
+    const float x = max3f(max3f(a, b, c), max3f(d, e, f), max3f(g, h, i));
+    const float mx = half_pair_max(max3f(x, k, fmaxf(v[14], v[15])));
+    const float mnew = fmaxf(m[j], mx);
+    const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * c2);  // 0 while m is -inf
+    l[j] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      o[0][j][r] *= alpha;
+      o[1][j][r] *= alpha;
+    }
+    m[j] = mnew;
   }
-#endif
 }
+
+// VALU phase of page j: mask its empty slots, turn the scores into P (bf16)
+// against the current running max and add the row sums.  The max is not
+// looked at unless some lane's sum over its 32 keys exceeds 2^kSumLimitLog2
+// (or is inf: the first page, while m is still -inf); only then is it raised
+// to the page max, O and l rescaled and P recomputed.  Every p is therefore
+// at most 2^kSumLimitLog2, far from fp32 overflow in O and l, and since the
+// max only grows from values that occurred, P keeps bf16's relative
+// precision.  Every page holds at least one visible key for every row, so
+// the raised max is finite.
+constexpr uint32_t kSumLimitBits = 0x47800000u;  // 2^16 as fp32 bits; inf and NaN compare above
 
 template <int NJ>
-__device__ __forceinline__ void pv_tile(const uint16_t* sVb, int kt, const bf16x8 (&pf)[NJ][2],
-                                        f32x16 (&o)[2][NJ], int l32, int hf) {
-  constexpr int LR = 72;
+__device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], int valid, float (&m)[NJ],
+                                           float (&l)[NJ], f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4],
+                                           float c2, int hf) {
+  if (valid < kPage) mask_page<NJ>(sc, valid, hf);
+  float psum[NJ];
+  page_exp<NJ>(sc, m, pf, psum, c2);
+  bool big = false;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int kc = kt * 2 + hh;
+  for (int j = 0; j < NJ; ++j) big |= __builtin_bit_cast(uint32_t, psum[j]) > kSumLimitBits;
+  if (__any(big)) {
+    raise_max<NJ>(sc, m, l, o, c2);
+    page_exp<NJ>(sc, m, pf, psum, c2);
+  }
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sVb[(dt * 32 + l32) * LR + kc * 16 + hf * 8]);
+  for (int j = 0; j < NJ; ++j) l[j] += psum[j];
+}
+
+// Issue the copy of physical page pg into ring slot `slot` (K and V tiles):
+// lane l of wave w fetches the 16-byte chunk that belongs at LDS position
+// 64w + l of the swizzled tile.
+__device__ __forceinline__ void stage_page(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems],
+                                           int slot, int pg, int h, int tid) {
+  const size_t off = ((size_t)pg * a.H + h) * (kPage * kHeadDim);
+  // the wave index is uniform: as a scalar the LDS destinations stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int row = wave * 8 + (lane >> 3), pc = lane & 7;
+  const int src = row * 64 + ((pc ^ ((row >> 1) & 7)) << 3);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.kpool) + off + src;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.vpool) + off + src;
+  __builtin_amdgcn_global_load_lds(kp, &ring[slot][wave * 512], 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(vp, &ring[kRing + slot][wave * 512], 16, 0, 0);
+}
+
+// MFMA phase of page j: PV of page j-1 (P from the previous VALU phase, V^T
+// from slot sv) and QK^T of page j (K from slot sk).
+template <int NJ>
+__device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* sv, bool pv,
+                                           const bf16x8 (&qf)[NJ][4], const bf16x8 (&pf)[NJ][4],
+                                           f32x16 (&o)[2][NJ], f32x16 (&sc)[2][NJ], int l32, int hf) {
+  if (pv) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][hh], o[dt][j], 0, 0, 0);
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sv[swz(dt * 32 + l32, kc * 2 + hf)]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kc], o[dt][j], 0, 0, 0);
+      }
+    }
+  }
+  // PV and QK^T in program order: interleaving them keeps P, the new scores
+  // and both operand sets live at once, more than 256 registers
+  __builtin_amdgcn_sched_barrier(0);
+  if (sk != nullptr) {
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = kt * 32 + l32;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[swz(row, c * 2 + hf)]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          sc[kt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[kt][j], 0, 0, 0);
+      }
     }
   }
 }
 
-// NW waves of 64 lanes; wave w owns query rows [w*32*NJ, (w+1)*32*NJ) of the
-// 512-row block as NJ tiles of 32 rows (NW * NJ = 16).
+// Write the appended frame's pages that fall in [p0, p1) to their pool pages:
+// K rows as they are, V rows transposed (through the ring slots) with slot s
+// at column swap23(s); slots past the frame's last row are zero.  Up to eight
+// pages go per round: all their rows are loaded first, so the round pays one
+// memory latency.  Only this workgroup reads these pages back in this launch
+// (workgroups of other query blocks with the same split write the same bytes),
+// so completing the stores and a workgroup-scope fence make them visible to
+// the copies that follow.
+constexpr int kFreshBatch = 8;
+
+__device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems], int p0,
+                                  int p1, int h, int tid) {
+  static_assert(2 * kRing >= kFreshBatch, "one LDS tile per page of a round");
+  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
+  const int f0 = npg - a.pl.fresh_cnt;
+  const int lo = p0 > f0 ? p0 : f0;
+  if (lo >= p1) return;  // uniform
+  const int H = a.H;
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
+  const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
+  uint16_t* kpool = reinterpret_cast<uint16_t*>(a.kpool);
+  uint16_t* vpool = reinterpret_cast<uint16_t*>(a.vpool);
+  const int row = tid >> 3, ch = tid & 7;  // 512 threads: one 16-byte chunk of a 64x64 tile each
+  const int col = swap23(row);
+  for (int b0 = lo; b0 < p1; b0 += kFreshBatch) {
+    uint4 kv[kFreshBatch], vv[kFreshBatch];
+#pragma unroll
+    for (int u = 0; u < kFreshBatch; ++u) {
+      const int j = b0 + u - f0;
+      const int valid = (j == a.pl.ppf - 1) ? a.pl.f_last_valid : kPage;
+      kv[u] = make_uint4(0u, 0u, 0u, 0u);
+      vv[u] = kv[u];
+      if (b0 + u < p1 && row < valid) {
+        const size_t src = ((size_t)(j * kPage + row) * H + h) * kHeadDim + ch * 8;
+        kv[u] = *reinterpret_cast<const uint4*>(kin + src);
+        vv[u] = *reinterpret_cast<const uint4*>(vin + src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFreshBatch; ++u) {
+      if (b0 + u < p1) {
+        const int pg = a.fresh.p[b0 + u - f0];
+        const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
+        *reinterpret_cast<uint4*>(kpool + off + row * 64 + ch * 8) = kv[u];
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ring[u][(ch * 8 + e) * 64 + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kFreshBatch; ++u) {
+      if (b0 + u < p1) {
+        const int pg = a.fresh.p[b0 + u - f0];
+        const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
+        *reinterpret_cast<uint4*>(vpool + off + row * 64 + ch * 8) =
+            *reinterpret_cast<const uint4*>(&ring[u][row * 64 + ch * 8]);
+      }
+    }
+    __syncthreads();
+  }
+  GCA_WAIT_VMCNT(0);  // the pool stores have completed
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+}
+
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
-  constexpr int NJ = 16 / NW;
-  constexpr int NT = NW * 64;          // threads
-  constexpr int CPT = 512 / NT;        // 16-byte chunks of an 8 KB tile per thread
-  constexpr int D = kHeadDim, P = kPage, LR = 72;  // LDS row: 64 bf16 + 8 pad
-  constexpr int TILE = P * LR;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][TILE];
+  static_assert(NW == 8, "the staging layout assumes 512 threads");
+  constexpr int NJ = 2;
+  constexpr int D = kHeadDim;
+  __shared__ __attribute__((aligned(16))) uint16_t ring[2 * kRing][kTileElems];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hf = lane >> 5, l32 = lane & 31;
   int h, qb, s;
   decode_wg(a, h, qb, s);
@@ -356,13 +480,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   const int p0 = (int)((long long)npg * s / a.nsplit);
   const int p1 = (int)((long long)npg * (s + 1) / a.nsplit);
   if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
+  if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
 
   // Q^T fragments: tile j, d-chunk c: column q = 32j + l32, d = 16c + 8hf .. +7
   bf16x8 qf[NJ][4];
   const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = qb * kQBlock + wave * 32 * NJ + j * 32 + l32;
+    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -386,165 +511,64 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
     l[j] = 0.f;
   }
   const float c2 = a.scale_log2;
-  const float thr = kLazyRescaleLog2 / c2;  // in raw score units
 
-  uint16_t* kpool = reinterpret_cast<uint16_t*>(a.kpool);
-  uint16_t* vpool = reinterpret_cast<uint16_t*>(a.vpool);
-  const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
-  const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
+  // Ping-pong.  Every wave runs the same per-page sequence -- an MFMA phase
+  // (PV of page j-1, QK^T of page j), a barrier, a VALU phase (softmax of page
+  // j), a barrier -- but waves 4-7 (group B) start one barrier later than
+  // waves 0-3 (group A).  The two groups share the SIMDs one to one, so while
+  // one wave of a SIMD issues MFMAs the other works on the VALU.  Barriers
+  // count arrivals, not code positions: in global phase 2j group A is in its
+  // MFMA phase of page j and group B in its VALU phase of page j-1; in phase
+  // 2j+1 the roles swap.  In its VALU phase of page j a wave issues its part of
+  // the copy of page j+kAhead into the slot page j+kAhead-kRing left, and
+  // before the next barrier it waits for its part of page j+2: B reads page
+  // j+2 two phases after that barrier but A already one phase after it.
+  const bool grp_a = GCA_PINGPONG ? wave < 4 : true;
+  const int np = p1 - p0;  // >= 1: there are never more splits than pages
+  // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed
+  static_assert(kAhead == 4, "prologue stages four pages");
+  stage_page(a, ring, 0, page_id(a, p0), h, tid);
+  stage_page(a, ring, 1, page_id(a, p0 + 1 < p1 ? p0 + 1 : p1 - 1), h, tid);
+  stage_page(a, ring, 2, page_id(a, p0 + 2 < p1 ? p0 + 2 : p1 - 1), h, tid);
+  stage_page(a, ring, 3, page_id(a, p0 + 3 < p1 ? p0 + 3 : p1 - 1), h, tid);
+  int pg_ahead = page_id(a, p0 + kAhead < p1 ? p0 + kAhead : p1 - 1);
+  GCA_WAIT_VMCNT(2 * (kAhead - 2));
+  wg_barrier();
+  if (!grp_a) wg_barrier();  // group B runs one phase behind
 
-  auto info_of = [&](int i) {
-    PageInfo pi;
-    const int pg = map_page(a, i, pi.valid, pi.fj);
-    pi.off = ((size_t)pg * H + h) * (P * D);
-    return pi;
+  f32x16 sc[2][NJ];
+  bf16x8 pf[NJ][4];
+  auto page_step = [&](int jj, auto slot_c) {
+    constexpr int S = decltype(slot_c)::value;  // ring slot of page p0 + jj
+    const int j = p0 + jj;
+    mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], jj > 0, qf, pf, o, sc, l32, hf);
+    if (GCA_PINGPONG) wg_barrier();
+    stage_page(a, ring, (S + kAhead) % kRing, pg_ahead, h, tid);
+    pg_ahead = page_id(a, j + kAhead + 1 < p1 ? j + kAhead + 1 : p1 - 1);
+    valu_phase<NJ>(sc, page_valid(a, j), m, l, o, pf, c2, hf);
+    GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
+    wg_barrier();
   };
-  // chunk x of a tile = 16 bytes at element 8x: row x/8, column chunk x%8
-  auto load_k = [&](const PageInfo& pi, uint4 (&kv)[CPT]) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
-      if (pi.fj < 0) {
-        kv[u] = *reinterpret_cast<const uint4*>(kpool + pi.off + x * 8);
-      } else {
-        kv[u] = make_uint4(0u, 0u, 0u, 0u);
-        if (row < pi.valid)
-          kv[u] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pi.fj * P + row) * H + h) * D + ch * 8);
-        if (qb == 0) *reinterpret_cast<uint4*>(kpool + pi.off + x * 8) = kv[u];
-      }
-    }
-  };
-  auto load_v = [&](const PageInfo& pi, uint4 (&vv)[CPT]) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
-      vv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (pi.fj < 0) {
-        vv[u] = *reinterpret_cast<const uint4*>(vpool + pi.off + x * 8);
-        if (pi.valid < P) vv[u] = mask_vt_chunk(vv[u], ch, pi.valid);
-      } else if (row < pi.valid) {
-        vv[u] = *reinterpret_cast<const uint4*>(vin + ((size_t)(pi.fj * P + row) * H + h) * D + ch * 8);
-      }
-    }
-  };
-  auto store_k = [&](int b, const uint4 (&kv)[CPT]) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int x = tid + u * NT;
-      *reinterpret_cast<uint4*>(&sK[b][(x >> 3) * LR + (x & 7) * 8]) = kv[u];
-    }
-  };
-  auto store_v = [&](int b, const uint4 (&vv)[CPT], int fj) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int x = tid + u * NT, row = x >> 3, ch = x & 7;
-      if (fj < 0) {
-        *reinterpret_cast<uint4*>(&sV[b][row * LR + ch * 8]) = vv[u];
-      } else {  // rows of the input: transpose into V^T on the way
-        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-        const int col = swap23(row);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sV[b][(ch * 8 + e) * LR + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-      }
-    }
-  };
-
-  // prologue: K and V of page p0, K of page p0+1; the V buffer of "page
-  // p0-1" is zeroed so that the first PV of the loop (with P = 0) is a no-op
-  PageInfo pi0 = info_of(p0);
-  PageInfo pi1{P, -1, 0}, pi2{P, -1, 0};
-  {
-    uint4 kv[CPT], vv[CPT];
-    load_k(pi0, kv);
-    load_v(pi0, vv);
-    store_k(0, kv);
-    store_v(0, vv, pi0.fj);
-    if (p0 + 1 < p1) {
-      pi1 = info_of(p0 + 1);
-      load_k(pi1, kv);
-      store_k(1, kv);
-    }
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int x = tid + u * NT;
-      *reinterpret_cast<uint4*>(&sV[2][(x >> 3) * LR + (x & 7) * 8]) = make_uint4(0u, 0u, 0u, 0u);
-    }
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  using C4 = std::integral_constant<int, 4>;
+  using C5 = std::integral_constant<int, 5>;
+  static_assert(kRing == 6, "the loop is unrolled over six slots");
+  for (int jj = 0; jj < np; jj += kRing) {
+    page_step(jj, C0{});
+    if (jj + 1 < np) page_step(jj + 1, C1{});
+    if (jj + 2 < np) page_step(jj + 2, C2{});
+    if (jj + 3 < np) page_step(jj + 3, C3{});
+    if (jj + 4 < np) page_step(jj + 4, C4{});
+    if (jj + 5 < np) page_step(jj + 5, C5{});
   }
-  __syncthreads();
-
-  f32x16 s_cur[NJ], s_nxt[NJ];
-  bf16x8 p_cur[NJ][2], p_prev[NJ][2];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p_prev[j][hh][e] = (__bf16)0.0f;
-  qk_tile<NJ>(sK[0], 0, qf, s_cur, l32, hf);
-
-  int b0 = 0, b1 = 1, b2 = 2;  // buffers of pages i, i+1, i+2 (V of page i-1 is in b2)
-  // One page: tiles u = (i, 0) and (i, 1).  Each half: mask the tile whose
-  // QK^T was issued in the previous half, issue PV of the previous tile, move
-  // the running max, then one branch-free block with QK^T of the next tile on
-  // the MFMA pipe and the exponentials of this tile on the VALU.
-  auto page_step = [&](int i, auto has1_c, auto has2_c, auto masked_c) {
-    constexpr bool has1 = decltype(has1_c)::value, has2 = decltype(has2_c)::value;
-    constexpr bool masked = decltype(masked_c)::value;  // page i has empty slots
-    uint4 kn[CPT], vn[CPT];
-    if (has2) {
-      pi2 = info_of(i + 2);
-      load_k(pi2, kn);
-    }
-    if (has1) load_v(pi1, vn);
-    if (pi0.fj >= 0 && qb == 0) {  // the appended frame's V^T tile goes to its pool page
-#pragma unroll
-      for (int u = 0; u < CPT; ++u) {
-        const int x = tid + u * NT;
-        *reinterpret_cast<uint4*>(vpool + pi0.off + x * 8) =
-            *reinterpret_cast<const uint4*>(&sV[b0][(x >> 3) * LR + (x & 7) * 8]);
-      }
-    }
-    // half 0: tile (i, 0)
-    if (masked) mask_tile<NJ>(s_cur, pi0.valid, 0, hf);
-    pv_tile<NJ>(sV[b2], 1, p_prev, o, l32, hf);
-    softmax_max<NJ>(s_cur, m, l, o, c2, thr);
-    qk_tile<NJ>(sK[b0], 1, qf, s_nxt, l32, hf);
-    softmax_exp<NJ>(s_cur, m, l, p_cur, c2);
-    interleave_hint();
-    // half 1: tile (i, 1)
-    if (masked) mask_tile<NJ>(s_nxt, pi0.valid, 1, hf);
-    pv_tile<NJ>(sV[b0], 0, p_cur, o, l32, hf);
-    softmax_max<NJ>(s_nxt, m, l, o, c2, thr);
-    if (has1) qk_tile<NJ>(sK[b1], 0, qf, s_cur, l32, hf);
-    softmax_exp<NJ>(s_nxt, m, l, p_prev, c2);
-    interleave_hint();
-
-    if (has2) store_k(b2, kn);
-    if (has1) store_v(b1, vn, pi1.fj);
-    pi0 = pi1;
-    pi1 = pi2;
-    const int t0 = b0;
-    b0 = b1;
-    b1 = b2;
-    b2 = t0;
-    __syncthreads();
-  };
-  using T_ = std::integral_constant<bool, true>;
-  using F_ = std::integral_constant<bool, false>;
-  // full pages take a body without any masking code (no branch splits the
-  // MFMA/VALU block); the few partial pages (a frame's last page, the
-  // summary tail) take the masked body
-  int i = p0;
-  for (; i + 2 < p1; ++i) {
-    if (pi0.valid == P)
-      page_step(i, T_{}, T_{}, F_{});
-    else
-      page_step(i, T_{}, T_{}, T_{});
-  }
-  if (i + 1 < p1) page_step(i++, T_{}, F_{}, T_{});
-  page_step(i, F_{}, F_{}, T_{});
-  pv_tile<NJ>(sV[b2], 1, p_prev, o, l32, hf);  // tile (p1-1, 1)
+  // PV of the last page; group A then takes the barrier that group B took
+  // first, so both have passed the same number
+  mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], true, qf, pf, o, sc, l32, hf);
+  if (GCA_PINGPONG && grp_a) wg_barrier();
+  GCA_WAIT_VMCNT(0);  // no copy into LDS outlives the workgroup
 
   // epilogue
 #pragma unroll
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   const bool final_out = a.nsplit == 1;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = qb * kQBlock + wave * 32 * NJ + j * 32 + l32;
+    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
     if (final_out) {
       if (row < a.Lq) {
         const float inv = 1.f / l[j];
