@@ -11,6 +11,9 @@ constexpr int kHeadDim = 64;     // head dimension the kernels are written for
 constexpr int kQBlock = 512;     // query rows per bf16 attention workgroup (8 waves x 64)
 constexpr int kF32Rows = 256;    // query rows per fp32 attention workgroup
 constexpr int kTargetWgs = 256;  // one workgroup per MI355X compute unit
+// Logical pages one key split of the bf16 attention may hold: each workgroup
+// resolves its split's page ids into an LDS list of this many entries.
+constexpr int kListCap = 4096;
 constexpr int kMaxFramePages = 32;  // pages of one frame passed by value (F <= 2048)
 
 // Device-side state of one layer's cache, carved from the workspace.

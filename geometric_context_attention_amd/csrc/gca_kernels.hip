@@ -17,6 +17,7 @@
 // page policy itself is this library's.
 
 #include <math.h>
+#include <stddef.h>
 
 #include <type_traits>
 
@@ -132,21 +133,59 @@ __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, in
   return pg;
 }
 
-// Physical page of logical page i (loads through the constant space).
-__device__ __forceinline__ int page_id(const AttnArgs& a, int i) {
-  int valid, fj;
-  return map_page(a, i, valid, fj);
+// Page ids of the appended frame, read in place from the kernel's argument
+// block (the kernels below take one AttnArgs by value, which sits at the
+// start of that block).  A per-lane index into the by-value copy would make
+// the compiler move the whole argument block to scratch memory.
+__device__ __forceinline__ const_i32p fresh_page_ids() {
+  typedef const char __attribute__((address_space(4)))* const_bytep;
+  const const_bytep kargs = (const_bytep)__builtin_amdgcn_kernarg_segment_ptr();
+  return (const_i32p)(kargs + offsetof(AttnArgs, fresh) + offsetof(FramePages, p));
 }
 
-// Valid slots of logical page i (arithmetic only).
-__device__ __forceinline__ int page_valid(const AttnArgs& a, int i) {
+// Where logical page i's physical id comes from, for one lane (i may differ
+// across lanes): the table entry to load (always a valid address) and the
+// page's valid slots.
+__device__ __forceinline__ const_i32p page_source(const AttnArgs& a, int i, int& valid) {
   const PageList& pl = a.pl;
-  if (i < pl.a_cnt) return (i % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-  i -= pl.a_cnt;
-  if (i < pl.s_cnt) return (i == pl.s_cnt - 1) ? pl.s_last_valid : kPage;
-  i -= pl.s_cnt;
-  if (i < pl.w_cnt) return ((pl.w_first + i) % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
-  return (i - pl.w_cnt == pl.ppf - 1) ? pl.f_last_valid : kPage;
+  if (i < pl.a_cnt) {
+    valid = (i % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
+    return (const_i32p)a.ftab + i;
+  }
+  if ((i -= pl.a_cnt) < pl.s_cnt) {
+    valid = (i == pl.s_cnt - 1) ? pl.s_last_valid : kPage;
+    return (const_i32p)a.slist + i;
+  }
+  if ((i -= pl.s_cnt) < pl.w_cnt) {
+    const int e = pl.w_first + i;
+    valid = (e % pl.ppf == pl.ppf - 1) ? pl.f_last_valid : kPage;
+    return (const_i32p)a.ftab + e;
+  }
+  i -= pl.w_cnt;
+  valid = (i == pl.ppf - 1) ? pl.f_last_valid : kPage;
+  return fresh_page_ids() + i;
+}
+
+// List entry: physical page << 7 | valid slots; an id outside the pool (only
+// possible if the tables are corrupt) becomes page 0 with every slot masked.
+__device__ __forceinline__ uint32_t page_entry(const AttnArgs& a, int pg, int valid) {
+  if ((unsigned)pg >= (unsigned)a.pool) return 0u;
+  return ((uint32_t)pg << 7) | (uint32_t)valid;
+}
+
+// First logical page of key split s (s = nsplit gives npg).  Splits take
+// equal cost, a page of the appended frame counting 3/2 of another: the
+// workgroup holding those pages also writes them to the pool first.  Every
+// split keeps at least one page (nsplit <= npg).
+__host__ __device__ __forceinline__ int split_begin(const AttnArgs& a, int s) {
+  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
+  const int old_pages = npg - a.pl.fresh_cnt;
+  const long long cost = 2LL * old_pages + 3LL * a.pl.fresh_cnt;  // in half pages
+  const long long x = cost * s / a.nsplit;
+  int b = x <= 2LL * old_pages ? (int)(x / 2) : old_pages + (int)((x - 2LL * old_pages) / 3);
+  b = b > s ? b : s;
+  const int last = npg - (a.nsplit - s);
+  return b < last ? b : last;
 }
 
 // Workgroup index -> (head, query block, split).  Workgroups are dealt to the
@@ -206,8 +245,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef GCA_PINGPONG
 #define GCA_PINGPONG 1
 #endif
-constexpr int kRing = 6;       // LDS page slots
-constexpr int kAhead = 4;      // a wave stages page j + kAhead while it computes page j
+#ifndef GCA_RING
+#define GCA_RING 6
+#endif
+#ifndef GCA_AHEAD
+#define GCA_AHEAD 4
+#endif
+constexpr int kRing = GCA_RING;    // LDS page slots
+constexpr int kAhead = GCA_AHEAD;  // a wave stages page j + kAhead while it computes page j
 static_assert(kRing >= kAhead + 2, "a slot is refilled only after both wave groups have read it");
 constexpr int kTileElems = 4096;
 constexpr int kAttnWaves = 8;  // 512 threads, 2 waves per SIMD
@@ -242,9 +287,11 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 
 // visible by the explicit vmcnt wait before it, and the compiler is kept from
 // moving memory accesses across it.
 __device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int NJ>
@@ -403,9 +450,13 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
 // at column swap23(s); slots past the frame's last row are zero.  Up to eight
 // pages go per round: all their rows are loaded first, so the round pays one
 // memory latency.  Only this workgroup reads these pages back in this launch
-// (workgroups of other query blocks with the same split write the same bytes),
-// so completing the stores and a workgroup-scope fence make them visible to
-// the copies that follow.
+// (workgroups of other query blocks with the same split write the same
+// bytes), and wave w stores exactly the tile rows 8w .. 8w+7 that its own
+// copies later fetch (see stage_page), so the stores need no fence: the
+// copies of a wave issue after its stores, and the vector-memory counter the
+// page loop waits on completes in order, so every store has completed before
+// a copy issued after the next such wait.  The caller waits explicitly when
+// a written page is staged before the loop's first wait.
 constexpr int kFreshBatch = 8;
 
 __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems], int p0,
@@ -443,8 +494,12 @@ __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing]
         const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
         *reinterpret_cast<uint4*>(kpool + off + row * 64 + ch * 8) = kv[u];
         const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+        // V^T element (d, col) sits at chunk (col >> 3) ^ (d >> 3) of row d:
+        // the lanes of one store write rows d = 8ch + e, 1 KB apart, which
+        // the XOR moves to eight different bank groups
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ring[u][(ch * 8 + e) * 64 + col] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+        for (int e = 0; e < 8; ++e)
+          ring[u][(ch * 8 + e) * 64 + (((col >> 3) ^ ch) << 3) + (col & 7)] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
       }
     }
     __syncthreads();
@@ -454,14 +509,21 @@ __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing]
         const int pg = a.fresh.p[b0 + u - f0];
         const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
         *reinterpret_cast<uint4*>(vpool + off + row * 64 + ch * 8) =
-            *reinterpret_cast<const uint4*>(&ring[u][row * 64 + ch * 8]);
+            *reinterpret_cast<const uint4*>(&ring[u][row * 64 + ((ch ^ (row >> 3)) << 3)]);
       }
     }
-    __syncthreads();
+    __syncthreads();  // the tiles are free again
   }
-  GCA_WAIT_VMCNT(0);  // the pool stores have completed
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
+}
+
+// f(jj + S, slot S) for S = S0 .. N-1 while jj + S < np, with S a constant:
+// the ring loop is unrolled over its slots so every slot index is known.
+template <int S0, int N, class F>
+__device__ __forceinline__ void for_each_slot(int jj, int np, F& f) {
+  if constexpr (S0 < N) {
+    if (jj + S0 < np) f(jj + S0, std::integral_constant<int, S0>{});
+    for_each_slot<S0 + 1, N>(jj, np, f);
+  }
 }
 
 template <int NW>
@@ -469,7 +531,13 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   static_assert(NW == 8, "the staging layout assumes 512 threads");
   constexpr int NJ = 2;
   constexpr int D = kHeadDim;
-  __shared__ __attribute__((aligned(16))) uint16_t ring[2 * kRing][kTileElems];
+  // One LDS array holds the ring (tiles 0 .. 2*kRing-1) and the page list
+  // (the tiles after it): with a single LDS object the compiler can tell the
+  // ring slots apart and waits on the copies only where this code asks it to.
+  constexpr int kListTiles = kListCap * 4 / (kTileElems * 2);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kRing + kListTiles][kTileElems];
+  auto& ring = *reinterpret_cast<uint16_t(*)[2 * kRing][kTileElems]>(&lds[0][0]);
+  uint32_t* plist = reinterpret_cast<uint32_t*>(&lds[2 * kRing][0]);  // the split's pages, see page_entry
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hf = lane >> 5, l32 = lane & 31;
@@ -477,10 +545,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   decode_wg(a, h, qb, s);
   const int H = a.H;
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
-  const int p0 = (int)((long long)npg * s / a.nsplit);
-  const int p1 = (int)((long long)npg * (s + 1) / a.nsplit);
+  const int p0 = split_begin(a, s);
+  const int p1 = split_begin(a, s + 1);
   if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
-  if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
+  // The prologue issues its loads (the first list entries, Q, the appended
+  // frame's rows) before it waits on any of them.
+  // The split's pages are resolved once (p1 - p0 <= kListCap: the host picks
+  // enough splits); the loop then reads page ids from LDS instead of walking
+  // the page tables with scalar code.
+  int valid0;
+  const int raw0 = *page_source(a, p0 + tid < p1 ? p0 + tid : p1 - 1, valid0);
 
   // Q^T fragments: tile j, d-chunk c: column q = 32j + l32, d = 16c + 8hf .. +7
   bf16x8 qf[NJ][4];
@@ -496,6 +570,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
       qf[j][c] = __builtin_bit_cast(bf16x8, v);
     }
   }
+
+  const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
+  if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
+  if (p0 + tid < p1) plist[tid] = page_entry(a, raw0, valid0);
+  for (int i = p0 + tid + NW * 64; i < p1; i += NW * 64) {
+    int valid;
+    const int raw = *page_source(a, i, valid);
+    plist[i - p0] = page_entry(a, raw, valid);
+  }
+  __syncthreads();
+  auto page_id = [&](int i) { return (int)(__builtin_amdgcn_readfirstlane(plist[i - p0]) >> 7); };
+  auto page_valid = [&](int i) { return (int)(__builtin_amdgcn_readfirstlane(plist[i - p0]) & 127u); };
 
   f32x16 o[2][NJ];
 #pragma unroll
@@ -525,13 +611,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   // j+2 two phases after that barrier but A already one phase after it.
   const bool grp_a = GCA_PINGPONG ? wave < 4 : true;
   const int np = p1 - p0;  // >= 1: there are never more splits than pages
-  // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed
-  static_assert(kAhead == 4, "prologue stages four pages");
-  stage_page(a, ring, 0, page_id(a, p0), h, tid);
-  stage_page(a, ring, 1, page_id(a, p0 + 1 < p1 ? p0 + 1 : p1 - 1), h, tid);
-  stage_page(a, ring, 2, page_id(a, p0 + 2 < p1 ? p0 + 2 : p1 - 1), h, tid);
-  stage_page(a, ring, 3, page_id(a, p0 + 3 < p1 ? p0 + 3 : p1 - 1), h, tid);
-  int pg_ahead = page_id(a, p0 + kAhead < p1 ? p0 + kAhead : p1 - 1);
+  // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed; a page
+  // this workgroup has just written is only staged after its stores completed
+  if (a.pl.fresh_cnt > 0 && f0 < p1 && f0 - p0 < kAhead) GCA_WAIT_VMCNT(0);
+#pragma unroll
+  for (int u = 0; u < kAhead; ++u) stage_page(a, ring, u, page_id(p0 + u < p1 ? p0 + u : p1 - 1), h, tid);
+  int pg_ahead = page_id(p0 + kAhead < p1 ? p0 + kAhead : p1 - 1);
   GCA_WAIT_VMCNT(2 * (kAhead - 2));
   wg_barrier();
   if (!grp_a) wg_barrier();  // group B runs one phase behind
@@ -544,26 +629,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
     mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], jj > 0, qf, pf, o, sc, l32, hf);
     if (GCA_PINGPONG) wg_barrier();
     stage_page(a, ring, (S + kAhead) % kRing, pg_ahead, h, tid);
-    pg_ahead = page_id(a, j + kAhead + 1 < p1 ? j + kAhead + 1 : p1 - 1);
-    valu_phase<NJ>(sc, page_valid(a, j), m, l, o, pf, c2, hf);
+    pg_ahead = page_id(j + kAhead + 1 < p1 ? j + kAhead + 1 : p1 - 1);
+    valu_phase<NJ>(sc, page_valid(j), m, l, o, pf, c2, hf);
     GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
     wg_barrier();
   };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
-  using C4 = std::integral_constant<int, 4>;
-  using C5 = std::integral_constant<int, 5>;
-  static_assert(kRing == 6, "the loop is unrolled over six slots");
-  for (int jj = 0; jj < np; jj += kRing) {
-    page_step(jj, C0{});
-    if (jj + 1 < np) page_step(jj + 1, C1{});
-    if (jj + 2 < np) page_step(jj + 2, C2{});
-    if (jj + 3 < np) page_step(jj + 3, C3{});
-    if (jj + 4 < np) page_step(jj + 4, C4{});
-    if (jj + 5 < np) page_step(jj + 5, C5{});
-  }
+  for (int jj = 0; jj < np; jj += kRing) for_each_slot<0, kRing>(jj, np, page_step);
   // PV of the last page; group A then takes the barrier that group B took
   // first, so both have passed the same number
   mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], true, qf, pf, o, sc, l32, hf);
@@ -620,8 +691,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   decode_wg(a, h, qb, s);
   const int H = a.H;
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
-  const int p0 = (int)((long long)npg * s / a.nsplit);
-  const int p1 = (int)((long long)npg * (s + 1) / a.nsplit);
+  const int p0 = split_begin(a, s);
+  const int p1 = split_begin(a, s + 1);
   if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
   const int row = qb * kF32Rows + threadIdx.x;
   const bool live = row < a.Lq;
@@ -843,6 +914,10 @@ hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int fr
 
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   const int grid = a.H * a.qblocks * a.nsplit;
+  // the bf16 kernel keeps its split's page list in LDS (the split count is
+  // chosen so it always fits; checked here before anything is launched)
+  for (int sp = 0; !f32 && sp < a.nsplit; ++sp)
+    if (split_begin(a, sp + 1) - split_begin(a, sp) > kListCap) return hipErrorInvalidValue;
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, dim3(grid), dim3(256), 0, st, a);
   else

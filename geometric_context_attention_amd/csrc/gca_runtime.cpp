@@ -49,11 +49,18 @@ struct Geometry {
 
 int query_rows(const gca_config& c) { return c.dtype == GCA_FP32 ? 256 : kQBlock; }
 
+// Key splits per (head, query block): enough workgroups to fill the chip,
+// at most max_splits if set, never more than there are pages, and never so
+// few that a split can hold more than kListCap pages (that bound wins over
+// max_splits).  The kernels weight the appended frame's pages (at most
+// kMaxFramePages) by 3/2 when cutting splits, so a split may get up to
+// (npg + fresh / 2) / s + 1 pages.
 int choose_splits(const gca_config& c, int qblocks, int64_t npg) {
   const int64_t base = (int64_t)c.num_heads * qblocks;
   int64_t s = cdiv(kTargetWgs, base);
   if (c.max_splits > 0 && s > c.max_splits) s = c.max_splits;
   if (s > npg) s = npg;
+  s = std::max<int64_t>(s, cdiv(npg + kMaxFramePages, kListCap - 1));
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -119,7 +126,7 @@ void make_geometry(const gca_config& c, Geometry& g) {
   for (int64_t L : lq) {
     const int qb = (int)cdiv(L, qr);
     const int64_t lq_pad = cdiv(L, kQBlock) * kQBlock;
-    const int s = choose_splits(c, qb, INT32_MAX);
+    const int s = choose_splits(c, qb, g.pool);  // no step sees more pages than the pool holds
     if (s > 1) {
       po = std::max(po, (size_t)c.num_heads * s * lq_pad * kHeadDim * 4);
       pml = std::max(pml, (size_t)c.num_heads * s * lq_pad * 8);
