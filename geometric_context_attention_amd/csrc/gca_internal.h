@@ -79,7 +79,7 @@ struct AttnArgs {
   // nsplit == 1: final outputs; else partials
   void* out;            // [Lq][H][D] in the stream dtype
   float* lse;           // [H][Lq] or null
-  float* part_o;        // [H][nsplit][Lq_pad][D]
+  void* part_o;         // [H][nsplit][Lq_pad][D]: fp32 O_s (fp32 path) or bf16 O_s / l_s (bf16 path)
   float2* part_ml;      // [H][nsplit][Lq_pad] (max of raw scores, sum of exp)
   int32_t Lq_pad;       // round_up(Lq, 512)
   int32_t pool;         // pages in the pool (entries outside [0, pool) are masked)

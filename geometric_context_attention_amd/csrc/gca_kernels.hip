@@ -666,15 +666,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
           }
         if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * a.scale + logf(l[j]);
       }
-    } else {
-      float* po = a.part_o + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+    } else if (row < a.Lq) {
+      // split partial: O / l rounded to bf16, with (m, l) in fp32
+      const float inv = 1.f / l[j];
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = dt * 32 + 8 * g + 4 * hf;
-          *reinterpret_cast<float4*>(po + d) =
-              make_float4(o[dt][j][4 * g + 0], o[dt][j][4 * g + 1], o[dt][j][4 * g + 2], o[dt][j][4 * g + 3]);
+          __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
+          __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
+          uint2 w;
+          w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
+          w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
+          *reinterpret_cast<uint2*>(po + d) = w;
         }
       if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
     }
@@ -766,7 +772,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     for (int d = 0; d < D; ++d) out[d] = o[d] * inv;
     if (a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = m * a.scale + logf(l);
   } else {
-    float* po = a.part_o + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+    float* po = reinterpret_cast<float*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
 #pragma unroll
     for (int d = 0; d < D; ++d) po[d] = o[d];
     a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m, l);
@@ -794,17 +800,35 @@ __device__ void merge_block(const AttnArgs& a, int h, int rb) {
   const float c2 = a.scale_log2;
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* po = a.part_o + ((size_t)h * ns * a.Lq_pad + row) * D + d4;
+  const size_t first = ((size_t)h * ns * a.Lq_pad + row) * D + d4, stride = (size_t)a.Lq_pad * D;
+  if (kF32) {
+    // unnormalised fp32 partials: split s adds 2^((m_s - M) c2) (O_s, l_s)
+    const float* po = reinterpret_cast<const float*>(a.part_o) + first;
 #pragma unroll 4
-  for (int s = 0; s < ns; ++s) {
-    const float2 v = ml[(size_t)s * a.Lq_pad];
-    const float w = exp2f((v.x - M) * c2);
-    L = __builtin_fmaf(w, v.y, L);
-    const float4 x = *reinterpret_cast<const float4*>(po + (size_t)s * a.Lq_pad * D);
-    acc.x = __builtin_fmaf(w, x.x, acc.x);
-    acc.y = __builtin_fmaf(w, x.y, acc.y);
-    acc.z = __builtin_fmaf(w, x.z, acc.z);
-    acc.w = __builtin_fmaf(w, x.w, acc.w);
+    for (int s = 0; s < ns; ++s) {
+      const float2 v = ml[(size_t)s * a.Lq_pad];
+      const float w = exp2f((v.x - M) * c2);
+      L = __builtin_fmaf(w, v.y, L);
+      const float4 x = *reinterpret_cast<const float4*>(po + s * stride);
+      acc.x = __builtin_fmaf(w, x.x, acc.x);
+      acc.y = __builtin_fmaf(w, x.y, acc.y);
+      acc.z = __builtin_fmaf(w, x.z, acc.z);
+      acc.w = __builtin_fmaf(w, x.w, acc.w);
+    }
+  } else {
+    // normalised bf16 partials O_s / l_s: split s weighs 2^((m_s - M) c2) l_s
+    const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o) + first;
+#pragma unroll 4
+    for (int s = 0; s < ns; ++s) {
+      const float2 v = ml[(size_t)s * a.Lq_pad];
+      const float w = exp2f((v.x - M) * c2) * v.y;
+      L += w;
+      const uint2 x = *reinterpret_cast<const uint2*>(po + s * stride);
+      acc.x = __builtin_fmaf(w, __builtin_bit_cast(float, x.x << 16), acc.x);
+      acc.y = __builtin_fmaf(w, __builtin_bit_cast(float, x.x & 0xffff0000u), acc.y);
+      acc.z = __builtin_fmaf(w, __builtin_bit_cast(float, x.y << 16), acc.z);
+      acc.w = __builtin_fmaf(w, __builtin_bit_cast(float, x.y & 0xffff0000u), acc.w);
+    }
   }
   const float inv = 1.f / L;
   const size_t o = ((size_t)row * a.H + h) * D + d4;

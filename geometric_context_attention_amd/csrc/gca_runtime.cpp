@@ -128,7 +128,7 @@ void make_geometry(const gca_config& c, Geometry& g) {
     const int64_t lq_pad = cdiv(L, kQBlock) * kQBlock;
     const int s = choose_splits(c, qb, g.pool);  // no step sees more pages than the pool holds
     if (s > 1) {
-      po = std::max(po, (size_t)c.num_heads * s * lq_pad * kHeadDim * 4);
+      po = std::max(po, (size_t)c.num_heads * s * lq_pad * kHeadDim * (c.dtype == GCA_FP32 ? 4 : 2));
       pml = std::max(pml, (size_t)c.num_heads * s * lq_pad * 8);
     }
   }
@@ -198,7 +198,7 @@ struct gca_ctx {
   char* ws = nullptr;
   std::vector<LayerDev> dev;
   std::vector<LayerHost> host;
-  float* part_o = nullptr;
+  void* part_o = nullptr;
   float2* part_ml = nullptr;
   bool f32 = false;
   // profiling
@@ -338,7 +338,7 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
     d.ctr = (int32_t*)m;
   }
   char* tail = c->ws + g.layer_stride * cfg->num_layers;
-  c->part_o = g.part_o_bytes ? (float*)tail : nullptr;
+  c->part_o = g.part_o_bytes ? (void*)tail : nullptr;
   c->part_ml = g.part_ml_bytes ? (float2*)(tail + g.part_o_bytes) : nullptr;
   rc = gca_reset(c, stream);
   if (rc != GCA_OK) {
