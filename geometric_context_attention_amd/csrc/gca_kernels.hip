@@ -294,16 +294,23 @@ __device__ __forceinline__ void wg_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Scores of the empty slots (key >= valid) of a page become -inf.  Keys of
+// register r of tile kt are 32kt + 8(r/4) + 4h + r%4 for lane half h, so the
+// slots form a suffix; a group of four registers is only looked at when the
+// (uniform) key range it covers reaches valid.
 template <int NJ>
 __device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (key >= valid) {
+    for (int g = 0; g < 4; ++g) {
+      if (kt * 32 + 8 * g + 7 >= valid) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) sc[kt][j][r] = -INFINITY;
+        for (int q = 0; q < 4; ++q) {
+          const bool dead = kt * 32 + 8 * g + 4 * hf + q >= valid;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) sc[kt][j][4 * g + q] = dead ? -INFINITY : sc[kt][j][4 * g + q];
+        }
       }
     }
 }
