@@ -31,6 +31,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+PEAK_CLOCK_GHZ = 2.4   # the clock the published peak is quoted at
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "GCA frames/s (12 layers, M=500,n=3,k=64,T=10k) + % of bf16 MFMA peak"
@@ -164,8 +165,10 @@ def main():
     fps = frames / elapsed
     attn_avg_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
     achieved = prof["attn_flop"] / (prof["attn_ms"] * 1e-3) / 1e12 if prof["attn_ms"] > 0 else 0.0
+    clock = prof["attn_clock_ghz"]
     log(f"{fps:.1f} frames/s; attention {prof['attn_launches']} launches, avg {attn_avg_ms * 1e3:.1f} us, "
-        f"{achieved:.1f} TFLOP/s; attention share of wall {prof['attn_ms'] / 1e3 / elapsed:.2%}")
+        f"{achieved:.1f} TFLOP/s; attention share of wall {prof['attn_ms'] / 1e3 / elapsed:.2%}; "
+        f"shader clock {clock:.2f} GHz")
 
     result = {
         "metric": METRIC,
@@ -196,6 +199,10 @@ def main():
             "launches": prof["attn_launches"],
             "algorithmic_flop_per_launch": prof["attn_flop"] / max(prof["attn_launches"], 1),
             "algorithmic_kv_bytes_per_launch": prof["attn_kv_bytes"] / max(prof["attn_launches"], 1),
+            # the peak assumes 2.4 GHz; the same peak at the clock measured
+            # inside the timed launches
+            "clock_ghz": round(clock, 3),
+            "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
         },
     }
     stack.close()

@@ -58,7 +58,8 @@ class gca_state_host(ctypes.Structure):
 
 class gca_profile(ctypes.Structure):
     _fields_ = [("attn_ms", ctypes.c_double), ("attn_launches", ctypes.c_int64),
-                ("attn_flop", ctypes.c_double), ("attn_kv_bytes", ctypes.c_double)]
+                ("attn_flop", ctypes.c_double), ("attn_kv_bytes", ctypes.c_double),
+                ("attn_clock_ghz", ctypes.c_double)]
 
 
 class GcaError(RuntimeError):

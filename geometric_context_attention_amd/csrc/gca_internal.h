@@ -83,6 +83,9 @@ struct AttnArgs {
   float2* part_ml;      // [H][nsplit][Lq_pad] (max of raw scores, sum of exp)
   int32_t Lq_pad;       // round_up(Lq, 512)
   int32_t pool;         // pages in the pool (entries outside [0, pool) are masked)
+  // profiling: workgroup 0 adds its duration in shader cycles to clock[0] and
+  // in 100 MHz reference ticks to clock[1] (null: not sampled)
+  unsigned long long* clock;
 };
 
 // Moving frame `frame` (pages `src`) into the trajectory memory: its S

@@ -550,6 +550,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   const int hf = lane >> 5, l32 = lane & 31;
   int h, qb, s;
   decode_wg(a, h, qb, s);
+  const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int H = a.H;
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = split_begin(a, s);
@@ -691,6 +692,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
         }
       if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
     }
+  }
+  if (a.clock != nullptr && blockIdx.x == 0 && tid == 0) {
+    atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
+    atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
   }
 }
 

@@ -32,6 +32,8 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr size_t kClockBytes = 256;  // profiling counters at the end of the workspace
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Derived sizes and workspace layout of a configuration.
@@ -134,7 +136,7 @@ void make_geometry(const gca_config& c, Geometry& g) {
   }
   g.part_o_bytes = align256(po);
   g.part_ml_bytes = align256(pml);
-  g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes;
+  g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes + kClockBytes;
   g.scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
 }
 
@@ -200,6 +202,8 @@ struct gca_ctx {
   std::vector<LayerHost> host;
   void* part_o = nullptr;
   float2* part_ml = nullptr;
+  unsigned long long* clock = nullptr;  // [2] device: shader cycles, reference ticks
+  unsigned long long clock_base[2] = {0, 0};
   bool f32 = false;
   // profiling
   bool prof = false;
@@ -259,6 +263,7 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.part_ml = c->part_ml;
   a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
   a.pool = c->g.pool;
+  a.clock = c->prof ? c->clock : nullptr;
   EventPair* ep = nullptr;
   if (c->prof) {
     ep = &c->ev[c->ev_next];
@@ -340,6 +345,7 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
   char* tail = c->ws + g.layer_stride * cfg->num_layers;
   c->part_o = g.part_o_bytes ? (void*)tail : nullptr;
   c->part_ml = g.part_ml_bytes ? (float2*)(tail + g.part_o_bytes) : nullptr;
+  c->clock = (unsigned long long*)(tail + g.part_o_bytes + g.part_ml_bytes);
   rc = gca_reset(c, stream);
   if (rc != GCA_OK) {
     delete c;
@@ -560,6 +566,10 @@ int gca_profile_enable(gca_ctx* c, int32_t on) {
     for (EventPair& e : c->ev) e.pending = false;
     c->attn_ms = c->attn_flop = c->attn_bytes = 0;
     c->attn_launches = 0;
+    // the clock counters only ever grow: remember where they stand
+    hipError_t r = hipDeviceSynchronize();
+    if (r == hipSuccess) r = hipMemcpy(c->clock_base, c->clock, sizeof(c->clock_base), hipMemcpyDeviceToHost);
+    if (r != hipSuccess) return hip_fail(r, "reading the clock counters");
   }
   c->prof = on != 0;
   return GCA_OK;
@@ -575,6 +585,12 @@ int gca_profile_read(gca_ctx* c, gca_profile* out) {
   out->attn_launches = c->attn_launches;
   out->attn_flop = c->attn_flop;
   out->attn_kv_bytes = c->attn_bytes;
+  out->attn_clock_ghz = 0.0;
+  unsigned long long now[2];
+  hipError_t r = hipMemcpy(now, c->clock, sizeof(now), hipMemcpyDeviceToHost);
+  if (r != hipSuccess) return hip_fail(r, "reading the clock counters");
+  const unsigned long long cyc = now[0] - c->clock_base[0], ticks = now[1] - c->clock_base[1];
+  if (ticks > 0) out->attn_clock_ghz = 0.1 * (double)cyc / (double)ticks;
   return GCA_OK;
 }
 

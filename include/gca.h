@@ -164,10 +164,13 @@ typedef struct {
   int64_t attn_launches;
   double attn_flop;      /* summed algorithmic flop of those launches */
   double attn_kv_bytes;  /* summed algorithmic K/V bytes read by those launches */
+  double attn_clock_ghz; /* shader clock during the bf16 attention launches, from
+                            the cycle and 100 MHz reference counters that one
+                            workgroup per launch samples; 0 if none ran */
 } gca_profile;
 
 /* Enable (1) or disable (0) HIP-event timing of every attention launch of
- * the context; enabling clears the accumulators. */
+ * the context; enabling clears the accumulators (and waits for the device). */
 int gca_profile_enable(gca_ctx* ctx, int32_t on);
 
 /* Wait for the timed launches to finish and return the accumulators. */
