@@ -34,7 +34,7 @@ class gca_config(ctypes.Structure):
                 ("k_window", ctypes.c_int32), ("max_frames", ctypes.c_int32),
                 ("page_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("pool_pages", ctypes.c_int32),
-                ("max_splits", ctypes.c_int32)]
+                ("max_splits", ctypes.c_int32), ("keyframe_interval", ctypes.c_int32)]
 
 
 class gca_plan_info(ctypes.Structure):
@@ -116,9 +116,10 @@ def _check(rc: int):
 
 def make_config(*, num_layers=1, num_heads, head_dim=64, image_tokens, summary_tokens=6,
                 n_anchor=3, k_window, max_frames, page_tokens=64, dtype=GCA_BF16, scale=0.0,
-                pool_pages=0, max_splits=0) -> gca_config:
+                pool_pages=0, max_splits=0, keyframe_interval=1) -> gca_config:
     return gca_config(num_layers, num_heads, head_dim, image_tokens, summary_tokens, n_anchor,
-                      k_window, max_frames, page_tokens, dtype, scale, pool_pages, max_splits)
+                      k_window, max_frames, page_tokens, dtype, scale, pool_pages, max_splits,
+                      keyframe_interval)
 
 
 def _stream_ptr(stream):

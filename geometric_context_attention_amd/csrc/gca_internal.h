@@ -67,7 +67,7 @@ struct AttnArgs {
   FramePages fresh;     // page ids of the appended frame
   const void* k_in;     // [F][H][D] rows of the appended frame (fresh_cnt > 0)
   const void* v_in;
-  int32_t fresh_frame;  // its frame index
+  int32_t fresh_frame;  // its frame-table slot; -1: not a keyframe (attended, not cached)
   LayerDev L;           // for the bookkeeping of the append (workgroup 0)
   int32_t Lq;
   int32_t H;

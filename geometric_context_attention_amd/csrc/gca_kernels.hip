@@ -555,7 +555,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = split_begin(a, s);
   const int p1 = split_begin(a, s + 1);
-  if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
+  if (a.pl.fresh_cnt > 0 && a.fresh_frame >= 0 && blockIdx.x == 0) record_fresh_frame(a);
   // The prologue issues its loads (the first list entries, Q, the appended
   // frame's rows) before it waits on any of them.
   // The split's pages are resolved once (p1 - p0 <= kListCap: the host picks
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = split_begin(a, s);
   const int p1 = split_begin(a, s + 1);
-  if (a.pl.fresh_cnt > 0 && blockIdx.x == 0) record_fresh_frame(a);
+  if (a.pl.fresh_cnt > 0 && a.fresh_frame >= 0 && blockIdx.x == 0) record_fresh_frame(a);
   const int row = qb * kF32Rows + threadIdx.x;
   const bool live = row < a.Lq;
   const float* q = reinterpret_cast<const float*>(a.q);

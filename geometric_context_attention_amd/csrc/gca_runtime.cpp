@@ -86,6 +86,7 @@ int validate(const gca_config* c, std::string& why) {
   if (!(std::isfinite(c->scale) && c->scale >= 0.f)) { why = "scale must be finite and >= 0"; return GCA_E_INVALID_ARG; }
   if (c->pool_pages < 0) { why = "pool_pages must be >= 0"; return GCA_E_INVALID_ARG; }
   if (c->max_splits < 0) { why = "max_splits must be >= 0"; return GCA_E_INVALID_ARG; }
+  if (c->keyframe_interval < 0) { why = "keyframe_interval must be >= 0"; return GCA_E_INVALID_ARG; }
   const int64_t F = (int64_t)c->image_tokens + c->summary_tokens;
   if ((int64_t)c->n_anchor * F > (1 << 24)) { why = "anchor block too large"; return GCA_E_INVALID_ARG; }
   const int64_t ppf = cdiv(F, kPage);
@@ -97,11 +98,25 @@ int validate(const gca_config* c, std::string& why) {
 // Peak pages of a max_frames stream: anchors + window + current frame +
 // summary pages at the last eviction (the tail page is taken before the
 // evicted frame's pages are freed).
+int64_t interval(const gca_config& c) { return c.keyframe_interval > 1 ? c.keyframe_interval : 1; }
+
+// Keyframes among frames n .. t-1 (frame n + j*m is one).
+int64_t keyframes_before(const gca_config& c, int64_t t) {
+  return t <= c.n_anchor ? 0 : cdiv(t - c.n_anchor, interval(c));
+}
+
+bool is_keyframe(const gca_config& c, int64_t t) {
+  return t < c.n_anchor || (t - c.n_anchor) % interval(c) == 0;
+}
+
 int64_t peak_pages(const gca_config& c, int ppf) {
+  // Window and trajectory memory only grow, so the last step needs the most
+  // pages: its own frame's pages, the window it sees, and the summary pages
+  // including the one a final eviction takes before freeing.
   const int64_t n = c.n_anchor, k = c.k_window, T = c.max_frames;
-  const int64_t wmax = std::min<int64_t>(k, T - 1 - n);  // -1 when T == n
+  const int64_t wmax = T > n ? std::min<int64_t>(k, keyframes_before(c, T - 1)) : -1;
   const int64_t full = (n + wmax + 1) * ppf;
-  const int64_t traj = std::max<int64_t>(0, T - n - k);
+  const int64_t traj = std::max<int64_t>(0, keyframes_before(c, T) - k);
   return full + cdiv(traj * c.summary_tokens, kPage);
 }
 
@@ -112,7 +127,7 @@ void make_geometry(const gca_config& c, Geometry& g) {
   const int64_t peak = peak_pages(c, g.ppf);
   g.pool = c.pool_pages > 0 ? c.pool_pages : (int)peak;
   g.words = (int)cdiv(g.pool, 32);
-  const int64_t traj_max = std::max<int64_t>(0, (int64_t)c.max_frames - c.n_anchor - c.k_window);
+  const int64_t traj_max = std::max<int64_t>(0, keyframes_before(c, c.max_frames) - c.k_window);
   g.max_sum_pages = (int)std::max<int64_t>(1, cdiv(traj_max * c.summary_tokens, kPage));
   g.ftab_entries = (int64_t)c.max_frames * g.ppf;
   g.eb = c.dtype == GCA_FP32 ? 4 : 2;
@@ -145,7 +160,8 @@ void make_geometry(const gca_config& c, Geometry& g) {
 // which write the device copy of the table; both copies evolve identically.
 struct LayerHost {
   bool streaming = false;
-  int frames = 0;  // frames appended
+  int next = 0;    // next frame index of the stream
+  int frames = 0;  // frames appended to the cache (frame-table slots used)
   int traj = 0;    // frames in trajectory memory
   int used = 0;    // pages in use
   int hint = 0;    // no page below this index is free
@@ -155,7 +171,7 @@ struct LayerHost {
 
   void init(const Geometry& g) {
     streaming = false;
-    frames = traj = used = hint = 0;
+    next = frames = traj = used = hint = 0;
     bits.assign((size_t)g.words, 0u);
     ftab.assign((size_t)g.ftab_entries, -1);
     slist.assign((size_t)g.max_sum_pages, -1);
@@ -398,6 +414,7 @@ int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, con
   if (rc != GCA_OK) return rc;
   hs.streaming = true;
   hs.frames = cfg.n_anchor;
+  hs.next = cfg.n_anchor;
   hs.traj = 0;
   return GCA_OK;
 }
@@ -412,22 +429,29 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
   const gca_config& cfg = c->cfg;
   const Geometry& g = c->g;
   const int n = cfg.n_anchor, kw = cfg.k_window, S = cfg.summary_tokens;
-  const int t = hs.frames;
+  const int t = hs.next;
   if (t >= cfg.max_frames) return fail(GCA_E_OUT_OF_PAGES, "stream reached max_frames; reset first");
-  const int w = std::min(kw, t - n);
-  const bool evict = (int64_t)t - kw >= n;
+  // Frame t is appended to frame-table slot hs.frames if it is a keyframe;
+  // the window is the last w cached keyframes (slots hs.frames-w .. hs.frames-1).
+  const bool key = is_keyframe(cfg, t);
+  const int w = std::min(kw, hs.frames - n);
+  const bool evict = key && hs.frames + 1 - n > kw;
   const int nsp = (int)cdiv((int64_t)S * hs.traj, kPage);
   const int new_sum = evict ? (int)(cdiv((int64_t)S * (hs.traj + 1), kPage) - nsp) : 0;
   if ((int64_t)hs.used + g.ppf + new_sum > g.pool)
     return fail(GCA_E_OUT_OF_PAGES, "page pool exhausted at frame " + std::to_string(t));
   hipStream_t st = (hipStream_t)stream;
-  // pages of frame t (lowest free first); then, if frame t-k leaves the
-  // window, a new summary page (before its pages are freed)
+  // pages of frame t (lowest free first; a non-keyframe gives them back at
+  // the end of the step); then, if a keyframe leaves the window, a new
+  // summary page (before its pages are freed)
+  const int slot = hs.frames;
   FramePages fresh{};
-  hs.alloc_frame(t, g.ppf, g.pool, fresh);
+  hs.alloc_frame(slot, g.ppf, g.pool, fresh);
+  if (!key)
+    for (int j = 0; j < g.ppf; ++j) hs.ftab[(size_t)slot * g.ppf + j] = -1;
   EvictPlan ev{};
   if (evict) {
-    const int fe = t - kw;
+    const int fe = slot - kw;  // the oldest window keyframe once frame t is in
     ev.frame = fe;
     ev.ppf = g.ppf;
     ev.S = S;
@@ -446,16 +470,21 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
   pl.a_cnt = n * g.ppf;
   pl.s_cnt = nsp;
   pl.s_last_valid = nsp > 0 ? (int)((int64_t)S * hs.traj - (int64_t)(nsp - 1) * kPage) : kPage;
-  pl.w_first = (t - w) * g.ppf;
+  pl.w_first = (hs.frames - w) * g.ppf;
   pl.w_cnt = w * g.ppf;
   pl.fresh_cnt = g.ppf;
   pl.ppf = g.ppf;
   pl.f_last_valid = g.f_last_valid;
   const int64_t keys = (int64_t)(n + w + 1) * g.F + (int64_t)S * hs.traj;
-  rc = run_step_kernels(c, layer, q, k, v, out, lse, g.F, pl, fresh, t, evict ? &ev : nullptr,
-                        keys, st);
+  rc = run_step_kernels(c, layer, q, k, v, out, lse, g.F, pl, fresh, key ? slot : -1,
+                        evict ? &ev : nullptr, keys, st);
   if (rc != GCA_OK) return rc;
-  hs.frames = t + 1;
+  hs.next = t + 1;
+  if (!key) {
+    for (int j = 0; j < g.ppf; ++j) hs.release(fresh.p[j]);
+    return GCA_OK;
+  }
+  hs.frames = slot + 1;
   if (evict) {
     for (int j = 0; j < g.ppf; ++j) {
       hs.release(ev.src.p[j]);
@@ -496,12 +525,14 @@ int gca_plan(const gca_config* cfg, int32_t t, gca_plan_info* out) {
     p.used_pages_after = (int32_t)(n * g.ppf);
   } else {
     Lq = F;
-    const int64_t w = std::min<int64_t>(k, t - n);
-    const int64_t traj = std::max<int64_t>(0, t - n - k);
+    const int64_t kb = keyframes_before(*cfg, t);
+    const int64_t w = std::min<int64_t>(k, kb);
+    const int64_t traj = std::max<int64_t>(0, kb - k);
     p.keys = (n + w + 1) * F + S * traj;
     npg = n * g.ppf + cdiv(S * traj, kPage) + (w + 1) * g.ppf;
-    const int64_t wa = std::min<int64_t>(k, t - n + 1);
-    const int64_t traj_after = t + 1 - n - wa;
+    const int64_t ka = kb + (is_keyframe(*cfg, t) ? 1 : 0);
+    const int64_t wa = std::min<int64_t>(k, ka);
+    const int64_t traj_after = ka - wa;
     p.cached_after = (n + wa) * F + S * traj_after;
     p.used_pages_after = (int32_t)((n + wa) * g.ppf + cdiv(S * traj_after, kPage));
   }

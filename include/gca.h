@@ -70,6 +70,10 @@ typedef struct {
   float scale;            /* softmax scale; 0 means 1/sqrt(head_dim) */
   int32_t pool_pages;     /* 0: the exact peak a max_frames stream needs; else pool size */
   int32_t max_splits;     /* 0: automatic key-split count; else an upper bound (>= 1) */
+  int32_t keyframe_interval; /* m (deep dive §3.2): frame t >= n_anchor enters the cache only
+                                when (t - n_anchor) % m == 0; other frames are attended (they
+                                see the cache and themselves) but not appended.  The window
+                                counts cached keyframes.  0 or 1: every frame is cached. */
 } gca_config;
 
 typedef struct gca_ctx gca_ctx;
@@ -134,7 +138,9 @@ int gca_plan(const gca_config* cfg, int32_t t, gca_plan_info* out);
 
 /* ---- inspection (tests) and profiling ---- */
 typedef struct {
-  int32_t frames_appended; /* next frame index of the layer */
+  int32_t frames_appended; /* frames in the cache's frame table so far (anchors, then
+                              keyframes); equals the next frame index when every frame
+                              is a keyframe */
   int32_t n_traj;          /* frames in the trajectory memory */
   int32_t n_summary_pages;
   int32_t used_pages;

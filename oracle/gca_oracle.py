@@ -19,6 +19,13 @@ Visibility of key row (f, r) to a query row of frame i (rule ``is_visible``):
   rows of every older frame n .. i-k-1 (technical summary §2.2 frame-type
   table and §2.5 mask table; paper-to-code map §二 2.3).  Nothing later
   than i is visible.
+* Keyframe interval m >= 1 (deep dive §3.2, the streaming loop, and §3.3):
+  frame i >= n is a keyframe when (i - n) is a multiple of m; the anchors are
+  always cached.  A frame that is not a keyframe is attended like any other
+  current frame but never enters the cache, so no later frame sees any of
+  its rows.  The window holds the k most recent keyframes before i (it
+  counts cached keyframes, not video frames), and older keyframes keep only
+  their summary rows.  With m = 1 this is the rule above.
 
 Readings where the pages leave a step open (each is listed with its reason in
 the design notes of the repository):
@@ -58,8 +65,9 @@ class GcaShape:
 
     M: int  # image tokens per frame
     n: int  # anchor frames
-    k: int  # pose-reference window frames
+    k: int  # pose-reference window frames (keyframes in the cache)
     S: int = 6  # summary tokens per frame (1 camera + 1 anchor + 4 register)
+    m: int = 1  # keyframe interval: 1 appends every frame
 
     @property
     def F(self) -> int:
@@ -69,6 +77,11 @@ class GcaShape:
 # --------------------------------------------------------------------------
 # Mask
 # --------------------------------------------------------------------------
+
+def is_keyframe(f: int, shp: GcaShape) -> bool:
+    """True if frame f enters the cache (anchors always do)."""
+    return f < shp.n or shp.m <= 1 or (f - shp.n) % shp.m == 0
+
 
 def is_visible(i: int, f: int, r: int, shp: GcaShape) -> bool:
     """True if key row r of frame f is visible to query frame i."""
@@ -81,7 +94,10 @@ def is_visible(i: int, f: int, r: int, shp: GcaShape) -> bool:
         return True
     if f < n:  # anchor context: all rows
         return True
-    if f >= i - k:  # pose-reference window: all rows
+    if not is_keyframe(f, shp):  # never cached
+        return False
+    later = sum(1 for g in range(f + 1, i) if is_keyframe(g, shp))
+    if later < k:  # one of the k latest keyframes before i: all rows
         return True
     return r < S  # trajectory memory: summary rows only
 
@@ -108,8 +124,11 @@ def step_key_mask(t: int, shp: GcaShape) -> np.ndarray:
     if t < n:
         m = np.broadcast_to(f < n, (t + 1, F))
     else:
-        full = (f == t) | (f < n) | (f >= t - k)
-        m = full | (r < S)
+        kf = (f < n) | (shp.m <= 1) | ((f - n) % max(shp.m, 1) == 0)
+        upto = np.cumsum(kf[:, 0])  # keyframes among frames 0..f
+        later = (upto[t - 1] - upto)[:, None]  # keyframes strictly between f and t
+        full = (f == t) | (f < n) | (kf & (later < k))
+        m = full | (kf & (r < S))
     return np.ascontiguousarray(m).reshape(-1)
 
 

@@ -16,12 +16,18 @@ this model fixes one, and the device cache must reproduce it bit for bit:
   F - (ppf-1)*P valid slots.
 * Anchor initialisation appends frames 0..n-1 in order, each taking ppf
   pages in ascending order.
-* Step t appends frame t the same way.  Then, if t - k >= n, frame
-  e = t - k leaves the window: for r = 0..S-1 its summary row r is copied to
-  summary slot g = S*j + r, where j counts frames evicted before it; slot g
-  lives in page ``summary_pages[g // P]`` at position g % P, and a new
-  summary page (lowest free) is appended to that list when g // P reaches its
-  length.  Only after the copy are frame e's ppf pages freed.
+* Step t appends frame t the same way.  Then, if more than k keyframes after
+  the anchors are cached, the oldest of them, e, leaves the window: for
+  r = 0..S-1 its summary row r is copied to summary slot g = S*j + r, where j
+  counts frames evicted before it; slot g lives in page
+  ``summary_pages[g // P]`` at position g % P, and a new summary page (lowest
+  free) is appended to that list when g // P reaches its length.  Only after
+  the copy are frame e's ppf pages freed.  With keyframe interval 1 the frame
+  evicted at step t is t - k, once t - k >= n.
+* A step whose frame is not a keyframe (keyframe interval m > 1, deep dive
+  §3.2) still attends to its own rows: it takes ppf pages the same way (lowest
+  free first) for the duration of the step and frees them at its end, leaving
+  the cache as it was.
 * Reset frees everything.
 
 Parity status: the policy is this repository's own specification, pinned by
@@ -39,13 +45,13 @@ def pages_per_frame(F: int, P: int) -> int:
     return -(-F // P)
 
 
-def pool_pages_needed(n: int, k: int, F: int, S: int, P: int, max_frames: int) -> int:
+def pool_pages_needed(n: int, k: int, F: int, S: int, P: int, max_frames: int, m: int = 1) -> int:
     """Peak page count over a stream of max_frames frames (simulated)."""
-    m = PageModel(n=n, k=k, F=F, S=S, P=P, num_pages=10 ** 9, max_frames=max_frames)
-    m.anchor_init()
+    pm = PageModel(n=n, k=k, F=F, S=S, P=P, num_pages=10 ** 9, max_frames=max_frames, m=m)
+    pm.anchor_init()
     for t in range(n, max_frames):
-        m.step(t)
-    return m.peak_used
+        pm.step(t)
+    return pm.peak_used
 
 
 @dataclass
@@ -57,13 +63,15 @@ class PageModel:
     P: int
     num_pages: int
     max_frames: int
+    m: int = 1  # keyframe interval
     used: list = field(default_factory=list)  # sorted free-list is derived
-    frame_pages: dict = field(default_factory=dict)  # frame -> [pages]
+    frame_pages: dict = field(default_factory=dict)  # cached frame -> [pages]
     summary_pages: list = field(default_factory=list)
     summary_src: list = field(default_factory=list)  # slot g -> (frame, row)
     n_traj: int = 0
-    n_frames: int = 0  # frames appended so far (next frame index)
+    n_frames: int = 0  # frames processed so far (next frame index)
     peak_used: int = 0
+    transient: list = field(default_factory=list)  # pages of a non-keyframe step
 
     def __post_init__(self):
         self.ppf = pages_per_frame(self.F, self.P)
@@ -94,6 +102,20 @@ class PageModel:
         return [p in self._used for p in range(self.num_pages)]
 
     # -- operations --------------------------------------------------------
+    def is_keyframe(self, f: int) -> bool:
+        return f < self.n or self.m <= 1 or (f - self.n) % self.m == 0
+
+    def slot_of(self, f: int) -> int:
+        """Frame-table slot of cached frame f: anchors, then keyframes in order."""
+        return f if f < self.n else self.n + (f - self.n) // max(self.m, 1)
+
+    @property
+    def n_cached(self) -> int:
+        """Frames appended to the cache so far (anchors and keyframes)."""
+        if self.n_frames <= self.n:
+            return self.n_frames
+        return self.n + -(-(self.n_frames - self.n) // max(self.m, 1))
+
     def _append_frame(self, f: int) -> None:
         if f >= self.max_frames:
             raise ValueError("frame index beyond max_frames")
@@ -117,21 +139,36 @@ class PageModel:
         self.n_traj += 1
 
     def begin_step(self, t: int) -> None:
-        """Append frame t; the attention of step t reads the cache after this."""
+        """Append frame t (or give it transient pages if it is not a
+        keyframe); the attention of step t reads the cache after this."""
         if t != self.n_frames or t < self.n:
             raise RuntimeError("steps must follow anchor init in frame order")
-        self._append_frame(t)
+        if self.is_keyframe(t):
+            self._append_frame(t)
+        else:
+            if t >= self.max_frames:
+                raise ValueError("frame index beyond max_frames")
+            self.transient = [self._alloc() for _ in range(self.ppf)]
+            self.n_frames = t + 1
 
     def end_step(self, t: int) -> None:
-        """Evict frame t-k to the trajectory memory if it leaves the window."""
-        if t - self.k >= self.n:
-            self._evict(t - self.k)
+        """Evict the oldest window keyframe if more than k are cached; free a
+        non-keyframe's transient pages."""
+        if self.transient:
+            for p in self.transient:
+                self._free(p)
+            self.transient = []
+            return
+        window = sorted(f for f in self.frame_pages if f >= self.n)
+        if len(window) > self.k:
+            self._evict(window[0])
 
     def step(self, t: int) -> None:
         self.begin_step(t)
         self.end_step(t)
 
     def reset(self) -> None:
+        self.transient = []
         self._used.clear()
         self._free_hint = 0
         self.frame_pages.clear()
@@ -181,7 +218,11 @@ class PageModel:
                 continue
             for j, p in enumerate(self.frame_pages[f]):
                 out.append((p, self.P if j < self.ppf - 1 else last_valid))
-        assert t == max(self.frame_pages)
+        if self.transient:  # the current frame, not cached
+            for j, p in enumerate(self.transient):
+                out.append((p, self.P if j < self.ppf - 1 else last_valid))
+        else:
+            assert t == max(self.frame_pages)
         return out
 
 

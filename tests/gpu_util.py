@@ -58,7 +58,7 @@ def check_state(stack: G.GcaStack, layer: int, pm: PageModel, rows_of=None, rows
     """
     st = stack.export_state(layer)
     assert st["device_error"] == 0, f"device error flag {st['device_error']}"
-    assert st["frames_appended"] == pm.n_frames
+    assert st["frames_appended"] == pm.n_cached
     assert st["n_traj"] == pm.n_traj
     assert st["n_summary_pages"] == len(pm.summary_pages)
     assert st["used_pages"] == pm.used_pages
@@ -68,7 +68,7 @@ def check_state(stack: G.GcaStack, layer: int, pm: PageModel, rows_of=None, rows
     ft = st["frame_table"]
     exp = np.full_like(ft, -1)
     for f, pages in pm.frame_pages.items():
-        exp[f] = pages
+        exp[pm.slot_of(f)] = pages
     assert np.array_equal(ft, exp), "frame table differs"
     sp = st["summary_pages"]
     ns = len(pm.summary_pages)

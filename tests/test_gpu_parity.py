@@ -23,14 +23,15 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 
 def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scale=1.0,
-                state_every=1, check_bytes=True, key_offset_std=0.0):
+                state_every=1, check_bytes=True, key_offset_std=0.0, interval=1):
     """Stream T frames through every layer; compare each step with the oracle."""
     gdt, tdt = DT[mode]
     F = M + S
     cfg = G.make_config(num_layers=layers, num_heads=H, image_tokens=M, summary_tokens=S,
-                        n_anchor=n, k_window=k, max_frames=T, dtype=gdt, max_splits=max_splits)
+                        n_anchor=n, k_window=k, max_frames=T, dtype=gdt, max_splits=max_splits,
+                        keyframe_interval=interval)
     stack = G.GcaStack(cfg)
-    shp = GcaShape(M=M, n=n, k=k, S=S)
+    shp = GcaShape(M=M, n=n, k=k, S=S, m=interval)
     scale = 1 / math.sqrt(64)
     results = []
     for layer in range(layers):
@@ -42,7 +43,7 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
         o_ref, l_ref = go.stream_online(to64(q), to64(kx), to64(v), shp, scale)
         qd, kd, vd = q.cuda(), kx.cuda(), v.cuda()
         pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=G.gca_plan(cfg, 0)["pool_pages"],
-                       max_frames=T)
+                       max_frames=T, m=interval)
 
         def rows_of(f, rows):
             return kd[f, rows], vd[f, rows]
@@ -62,7 +63,7 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
             if (t - n) % state_every == 0 or t == T - 1:
                 check_state(stack, layer, pm, rows_of if check_bytes else None)
         results.append(worst)
-        say(f"  {mode} M={M} n={n} k={k} T={T} H={H} layer {layer}: worst max-abs {worst:.2e}")
+        say(f"  {mode} M={M} n={n} k={k} T={T} H={H} m={interval} layer {layer}: worst max-abs {worst:.2e}")
     stack.close()
     return results
 
@@ -210,3 +211,13 @@ def test_error_paths():
     with pytest.raises(ValueError):
         st.anchor_init(0, x, x, x)  # fp32 tensors for a bf16 context
     st.close()
+
+
+def test_fp32_keyframe_interval_full_state():
+    """Keyframe interval 3 (non-keyframes attended, not cached), fp32, state every step."""
+    _run_stream("fp32", M=32, n=3, k=4, T=48, H=2, interval=3)
+
+
+def test_bf16_keyframe_interval_ragged():
+    """Keyframe interval 2 with ragged frames and several splits, bf16."""
+    _run_stream("bf16", M=181, n=2, k=3, T=40, H=4, interval=2, state_every=5)
