@@ -85,6 +85,7 @@ _SIGS = {
     "gca_export_state": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(gca_state_host), _VP]),
     "gca_pool_views": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_size_t)]),
+    "gca_step_keyframe": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_profile_enable": (ctypes.c_int, [_VP, _I32]),
     "gca_profile_read": (ctypes.c_int, [_VP, ctypes.POINTER(gca_profile)]),
 }
@@ -169,6 +170,12 @@ def gca_step(ctx, layer, q, k, v, out, lse=None, stream=None):
     _check(lib().gca_step(ctx, layer, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
                           _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
                           _stream_ptr(stream)))
+
+
+def gca_step_keyframe(ctx, layer, q, k, v, out, lse=None, append=True, stream=None):
+    _check(lib().gca_step_keyframe(ctx, layer, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
+                                   _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
+                                   1 if append else 0, _stream_ptr(stream)))
 
 
 def gca_reset(ctx, stream=None):
@@ -259,13 +266,17 @@ class GcaStack:
         gca_anchor_init(self.ctx, layer, q, k, v, out, lse, stream)
         return out, lse
 
-    def step(self, layer, q, k, v, want_lse=True, out=None, lse=None, stream=None):
+    def step(self, layer, q, k, v, want_lse=True, out=None, lse=None, stream=None, append=None):
+        """One step; append=None follows the keyframe schedule, True/False decides."""
         shape = (self.F, self.cfg.num_heads, self.cfg.head_dim)
         for name, t in (("q", q), ("k", k), ("v", v)):
             _ptr(t, self.dtype, shape, name)
         if out is None:
             out, lse = self._outputs(self.F, q, want_lse)
-        gca_step(self.ctx, layer, q, k, v, out, lse, stream)
+        if append is None:
+            gca_step(self.ctx, layer, q, k, v, out, lse, stream)
+        else:
+            gca_step_keyframe(self.ctx, layer, q, k, v, out, lse, append, stream)
         return out, lse
 
     def reset(self, stream=None):

@@ -419,8 +419,10 @@ int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, con
   return GCA_OK;
 }
 
-int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
-             float* lse, void* stream) {
+namespace {
+// append: 1 cache frame t, 0 attend only, -1 follow the keyframe schedule
+int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
+              float* lse, int append, void* stream) {
   int rc = check_ctx_layer(c, layer);
   if (rc != GCA_OK) return rc;
   if (!q || !k || !v || !out) return fail(GCA_E_INVALID_ARG, "q, k, v and out must be non-NULL");
@@ -433,7 +435,7 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
   if (t >= cfg.max_frames) return fail(GCA_E_OUT_OF_PAGES, "stream reached max_frames; reset first");
   // Frame t is appended to frame-table slot hs.frames if it is a keyframe;
   // the window is the last w cached keyframes (slots hs.frames-w .. hs.frames-1).
-  const bool key = is_keyframe(cfg, t);
+  const bool key = append < 0 ? is_keyframe(cfg, t) : append != 0;
   const int w = std::min(kw, hs.frames - n);
   const bool evict = key && hs.frames + 1 - n > kw;
   const int nsp = (int)cdiv((int64_t)S * hs.traj, kPage);
@@ -493,6 +495,18 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
     hs.traj += 1;
   }
   return GCA_OK;
+}
+
+}  // namespace
+
+int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
+             float* lse, void* stream) {
+  return step_impl(c, layer, q, k, v, out, lse, -1, stream);
+}
+
+int gca_step_keyframe(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v,
+                      void* out, float* lse, int32_t append, void* stream) {
+  return step_impl(c, layer, q, k, v, out, lse, append != 0 ? 1 : 0, stream);
 }
 
 void gca_destroy(gca_ctx* c) {

@@ -97,17 +97,30 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
 int gca_anchor_init(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
                     void* out, float* lse, void* stream);
 
-/* One GCA step of `layer` for its next frame t (t = n, n+1, ...): append
- * frame t, attend over anchors + trajectory summaries + window frames t-k..t-1
- * + frame t itself (technical summary §2.2, §2.5), then, if t-k >= n, move
- * frame t-k's S summary rows into the trajectory memory and free its pages
- * (paper-to-code map §二 2.3).
+/* One GCA step of `layer` for its next frame t (t = n, n+1, ...): attend over
+ * anchors + trajectory summaries + the window (the k most recent cached
+ * keyframes; frames t-k..t-1 when every frame is a keyframe) + frame t itself
+ * (technical summary §2.2, §2.5).  If frame t is a keyframe (the config's
+ * keyframe_interval schedule, deep dive §3.2) it is appended; then, if more
+ * than k keyframes follow the anchors, the oldest one's S summary rows move
+ * into the trajectory memory and its pages are freed (paper-to-code map
+ * §二 2.3).  A frame that is not a keyframe leaves the cache unchanged.
  *   q, k, v: [M+S, H, D] (device);  out: [M+S, H, D] (device);
  *   lse: [H, M+S] fp32 or NULL.
  * GCA_E_BAD_STATE before anchor init; GCA_E_OUT_OF_PAGES when frame t would
  * exceed max_frames or the pool (checked on the host before any launch). */
 int gca_step(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
              void* out, float* lse, void* stream);
+
+/* gca_step with the keyframe decision made by the caller (technical summary
+ * §5.1 selects keyframes by an optical-flow threshold computed from the
+ * model's own predictions): append != 0 caches frame t, append == 0 only
+ * attends.  The pool is sized for the config's keyframe_interval schedule;
+ * caching more frames than that schedule can end in GCA_E_OUT_OF_PAGES
+ * (an interval of 0 or 1 sizes it for every frame).  gca_plan describes the
+ * schedule, not the caller's choices. */
+int gca_step_keyframe(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
+                      void* out, float* lse, int32_t append, void* stream);
 
 /* Free every page of every layer and return all layers to the empty state
  * (window reset of the windowed mode: paper-to-code map §五). */

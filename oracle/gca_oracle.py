@@ -25,7 +25,10 @@ Visibility of key row (f, r) to a query row of frame i (rule ``is_visible``):
   current frame but never enters the cache, so no later frame sees any of
   its rows.  The window holds the k most recent keyframes before i (it
   counts cached keyframes, not video frames), and older keyframes keep only
-  their summary rows.  With m = 1 this is the rule above.
+  their summary rows.  With m = 1 this is the rule above.  The keyframes may
+  also be given as an explicit set (the technical summary §5.1 picks them by
+  an optical-flow threshold on the model's own predictions); the rule is the
+  same with "keyframe" meaning "in the set".
 
 Readings where the pages leave a step open (each is listed with its reason in
 the design notes of the repository):
@@ -68,6 +71,7 @@ class GcaShape:
     k: int  # pose-reference window frames (keyframes in the cache)
     S: int = 6  # summary tokens per frame (1 camera + 1 anchor + 4 register)
     m: int = 1  # keyframe interval: 1 appends every frame
+    kf: frozenset | None = None  # explicit keyframes >= n (overrides m)
 
     @property
     def F(self) -> int:
@@ -80,7 +84,11 @@ class GcaShape:
 
 def is_keyframe(f: int, shp: GcaShape) -> bool:
     """True if frame f enters the cache (anchors always do)."""
-    return f < shp.n or shp.m <= 1 or (f - shp.n) % shp.m == 0
+    if f < shp.n:
+        return True
+    if shp.kf is not None:
+        return f in shp.kf
+    return shp.m <= 1 or (f - shp.n) % shp.m == 0
 
 
 def is_visible(i: int, f: int, r: int, shp: GcaShape) -> bool:
@@ -124,7 +132,10 @@ def step_key_mask(t: int, shp: GcaShape) -> np.ndarray:
     if t < n:
         m = np.broadcast_to(f < n, (t + 1, F))
     else:
-        kf = (f < n) | (shp.m <= 1) | ((f - n) % max(shp.m, 1) == 0)
+        if shp.kf is not None:
+            kf = (f < n) | np.isin(f, np.array(sorted(shp.kf), dtype=np.int64))
+        else:
+            kf = (f < n) | (shp.m <= 1) | ((f - n) % max(shp.m, 1) == 0)
         upto = np.cumsum(kf[:, 0])  # keyframes among frames 0..f
         later = (upto[t - 1] - upto)[:, None]  # keyframes strictly between f and t
         full = (f == t) | (f < n) | (kf & (later < k))

@@ -64,6 +64,7 @@ class PageModel:
     num_pages: int
     max_frames: int
     m: int = 1  # keyframe interval
+    keyframes: frozenset | None = None  # explicit keyframes >= n (overrides m)
     used: list = field(default_factory=list)  # sorted free-list is derived
     frame_pages: dict = field(default_factory=dict)  # cached frame -> [pages]
     summary_pages: list = field(default_factory=list)
@@ -103,18 +104,20 @@ class PageModel:
 
     # -- operations --------------------------------------------------------
     def is_keyframe(self, f: int) -> bool:
-        return f < self.n or self.m <= 1 or (f - self.n) % self.m == 0
+        if f < self.n:
+            return True
+        if self.keyframes is not None:
+            return f in self.keyframes
+        return self.m <= 1 or (f - self.n) % self.m == 0
 
     def slot_of(self, f: int) -> int:
         """Frame-table slot of cached frame f: anchors, then keyframes in order."""
-        return f if f < self.n else self.n + (f - self.n) // max(self.m, 1)
+        return sum(1 for g in range(f) if self.is_keyframe(g))
 
     @property
     def n_cached(self) -> int:
         """Frames appended to the cache so far (anchors and keyframes)."""
-        if self.n_frames <= self.n:
-            return self.n_frames
-        return self.n + -(-(self.n_frames - self.n) // max(self.m, 1))
+        return sum(1 for g in range(self.n_frames) if self.is_keyframe(g))
 
     def _append_frame(self, f: int) -> None:
         if f >= self.max_frames:

@@ -23,7 +23,7 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 
 def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scale=1.0,
-                state_every=1, check_bytes=True, key_offset_std=0.0, interval=1):
+                state_every=1, check_bytes=True, key_offset_std=0.0, interval=1, chosen=None):
     """Stream T frames through every layer; compare each step with the oracle."""
     gdt, tdt = DT[mode]
     F = M + S
@@ -31,7 +31,7 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
                         n_anchor=n, k_window=k, max_frames=T, dtype=gdt, max_splits=max_splits,
                         keyframe_interval=interval)
     stack = G.GcaStack(cfg)
-    shp = GcaShape(M=M, n=n, k=k, S=S, m=interval)
+    shp = GcaShape(M=M, n=n, k=k, S=S, m=interval, kf=chosen)
     scale = 1 / math.sqrt(64)
     results = []
     for layer in range(layers):
@@ -43,7 +43,7 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
         o_ref, l_ref = go.stream_online(to64(q), to64(kx), to64(v), shp, scale)
         qd, kd, vd = q.cuda(), kx.cuda(), v.cuda()
         pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=G.gca_plan(cfg, 0)["pool_pages"],
-                       max_frames=T, m=interval)
+                       max_frames=T, m=interval, keyframes=chosen)
 
         def rows_of(f, rows):
             return kd[f, rows], vd[f, rows]
@@ -56,7 +56,8 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
         check_state(stack, layer, pm, rows_of if check_bytes else None)
         worst = 0.0
         for t in range(n, T):
-            out, lse = stack.step(layer, qd[t], kd[t], vd[t])
+            out, lse = stack.step(layer, qd[t], kd[t], vd[t],
+                                  append=None if chosen is None else t in chosen)
             pm.step(t)
             ma, _ = check_outputs(out, o_ref[t], lse, l_ref[t], mode, f"layer {layer} step {t}")
             worst = max(worst, ma)
@@ -221,3 +222,10 @@ def test_fp32_keyframe_interval_full_state():
 def test_bf16_keyframe_interval_ragged():
     """Keyframe interval 2 with ragged frames and several splits, bf16."""
     _run_stream("bf16", M=181, n=2, k=3, T=40, H=4, interval=2, state_every=5)
+
+
+def test_bf16_caller_chosen_keyframes():
+    """Keyframes chosen per step by the caller (gca_step_keyframe), bf16, state checks."""
+    rng = np.random.default_rng(5)
+    chosen = frozenset(int(t) for t in range(3, 60) if rng.random() < 0.4)
+    _run_stream("bf16", M=120, n=3, k=4, T=60, H=4, chosen=chosen, state_every=3)

@@ -49,16 +49,22 @@ def test_interval_one_is_the_dense_rule():
         assert np.array_equal(go.step_key_mask(t, a), go.step_key_mask(t, b))
 
 
-@pytest.mark.parametrize("n,k,m", [(2, 2, 2), (1, 0, 3), (3, 1, 4), (2, 5, 3)])
+@pytest.mark.parametrize("n,k,m", [(2, 2, 2), (1, 0, 3), (3, 1, 4), (2, 5, 3), (2, 2, "set"), (1, 3, "set")])
 def test_stream_reduces_to_dense_stream_of_keyframes(n, k, m):
     T, M, S, H, D = 17, 3, 2, 2, 4
     F = M + S
-    rng = np.random.default_rng(100 * n + 10 * k + m)
+    rng = np.random.default_rng(100 * n + 10 * k + (7 if m == "set" else m))
     q, kx, v = (rng.standard_normal((T, F, H, D)) for _ in range(3))
     scale = 0.6
-    o_m, l_m = go.stream_online(q, kx, v, GcaShape(M=M, n=n, k=k, S=S, m=m), scale)
+    if m == "set":  # an arbitrary caller-chosen keyframe set
+        chosen = frozenset(int(f) for f in range(n, T) if rng.random() < 0.45)
+        shp = GcaShape(M=M, n=n, k=k, S=S, kf=chosen)
+        keyframes = [f for f in range(T) if f < n or f in chosen]
+    else:
+        shp = GcaShape(M=M, n=n, k=k, S=S, m=m)
+        keyframes = [f for f in range(T) if f < n or (f - n) % m == 0]
+    o_m, l_m = go.stream_online(q, kx, v, shp, scale)
     dense = GcaShape(M=M, n=n, k=k, S=S)
-    keyframes = [f for f in range(T) if f < n or (f - n) % m == 0]
     # keyframes: the dense stream over the keyframe subsequence
     o_d, l_d = go.stream_online(q[keyframes], kx[keyframes], v[keyframes], dense, scale)
     for j, f in enumerate(keyframes):
@@ -148,6 +154,14 @@ def test_planner_matches_oracle_with_keyframes(M, S, n, k, T, m):
         assert p["cached_after"] == go.cached_token_count(t, shp)
         assert p["used_pages_after"] == pm.used_pages
     assert p["pool_pages"] == pm.peak_used
+
+
+def test_explicit_set_equal_to_schedule_is_the_schedule():
+    n, m, T = 3, 4, 40
+    sched = GcaShape(M=5, n=n, k=3, S=2, m=m)
+    chosen = GcaShape(M=5, n=n, k=3, S=2, kf=frozenset(range(n, T, m)))
+    for t in range(n, T):
+        assert np.array_equal(go.step_key_mask(t, sched), go.step_key_mask(t, chosen))
 
 
 def test_negative_interval_rejected():
