@@ -86,6 +86,7 @@ _SIGS = {
     "gca_pool_views": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_size_t)]),
     "gca_step_keyframe": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
+    "gca_frame_attention": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_profile_enable": (ctypes.c_int, [_VP, _I32]),
     "gca_profile_read": (ctypes.c_int, [_VP, ctypes.POINTER(gca_profile)]),
 }
@@ -176,6 +177,12 @@ def gca_step_keyframe(ctx, layer, q, k, v, out, lse=None, append=True, stream=No
     _check(lib().gca_step_keyframe(ctx, layer, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
                                    _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
                                    1 if append else 0, _stream_ptr(stream)))
+
+
+def gca_frame_attention(ctx, q, k, v, out, lse=None, frames=1, stream=None):
+    _check(lib().gca_frame_attention(ctx, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
+                                     _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
+                                     frames, _stream_ptr(stream)))
 
 
 def gca_reset(ctx, stream=None):
@@ -277,6 +284,18 @@ class GcaStack:
             gca_step(self.ctx, layer, q, k, v, out, lse, stream)
         else:
             gca_step_keyframe(self.ctx, layer, q, k, v, out, lse, append, stream)
+        return out, lse
+
+    def frame_attention(self, q, k, v, want_lse=True, stream=None):
+        """Intra-frame attention of q, k, v [frames, M+S, H, D]."""
+        B = q.shape[0]
+        shape = (B, self.F, self.cfg.num_heads, self.cfg.head_dim)
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _ptr(t, self.dtype, shape, name)
+        out = torch.empty(shape, dtype=self.dtype, device=q.device)
+        lse = (torch.empty((B, self.cfg.num_heads, self.F), dtype=torch.float32, device=q.device)
+               if want_lse else None)
+        gca_frame_attention(self.ctx, q, k, v, out, lse, B, stream)
         return out, lse
 
     def reset(self, stream=None):

@@ -44,6 +44,7 @@ struct Geometry {
   size_t pool_bytes = 0;  // one pool (K or V) of one layer
   size_t meta_bytes = 0;  // bitmap + ftab + slist + ctr of one layer
   size_t part_o_bytes = 0, part_ml_bytes = 0;
+  size_t scratch_bytes = 0;  // one pool (K or V) of ppf pages for frame attention
   size_t layer_stride = 0;
   size_t total = 0;
   float scale = 0.f;
@@ -151,7 +152,9 @@ void make_geometry(const gca_config& c, Geometry& g) {
   }
   g.part_o_bytes = align256(po);
   g.part_ml_bytes = align256(pml);
-  g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes + kClockBytes;
+  g.scratch_bytes = align256((size_t)g.ppf * page_bytes);
+  g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes + kClockBytes +
+            2 * g.scratch_bytes;
   g.scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
 }
 
@@ -219,6 +222,7 @@ struct gca_ctx {
   void* part_o = nullptr;
   float2* part_ml = nullptr;
   unsigned long long* clock = nullptr;  // [2] device: shader cycles, reference ticks
+  LayerDev scratch{};                   // ppf K/V pages for frame attention (pools only)
   unsigned long long clock_base[2] = {0, 0};
   bool f32 = false;
   // profiling
@@ -251,12 +255,13 @@ int harvest(gca_ctx* c, EventPair& e) {
 // splits and the eviction `ev` (if any) in a second launch.
 int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const void* v,
                      void* out, float* lse, int Lq, const PageList& pl, const FramePages& fresh,
-                     int fresh_frame, const EvictPlan* ev, int64_t keys, hipStream_t st) {
+                     int fresh_frame, const EvictPlan* ev, int64_t keys, hipStream_t st,
+                     bool use_scratch = false) {
   const gca_config& cfg = c->cfg;
   AttnArgs a{};
   a.q = q;
-  a.kpool = c->dev[layer].kpool;
-  a.vpool = c->dev[layer].vpool;
+  a.kpool = use_scratch ? c->scratch.kpool : c->dev[layer].kpool;
+  a.vpool = use_scratch ? c->scratch.vpool : c->dev[layer].vpool;
   a.ftab = c->dev[layer].ftab;
   a.slist = c->dev[layer].slist;
   a.pl = pl;
@@ -278,7 +283,7 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.part_o = c->part_o;
   a.part_ml = c->part_ml;
   a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
-  a.pool = c->g.pool;
+  a.pool = use_scratch ? c->g.ppf : c->g.pool;
   a.clock = c->prof ? c->clock : nullptr;
   EventPair* ep = nullptr;
   if (c->prof) {
@@ -362,6 +367,8 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
   c->part_o = g.part_o_bytes ? (void*)tail : nullptr;
   c->part_ml = g.part_ml_bytes ? (float2*)(tail + g.part_o_bytes) : nullptr;
   c->clock = (unsigned long long*)(tail + g.part_o_bytes + g.part_ml_bytes);
+  c->scratch.kpool = tail + g.part_o_bytes + g.part_ml_bytes + kClockBytes;
+  c->scratch.vpool = (char*)c->scratch.kpool + g.scratch_bytes;
   rc = gca_reset(c, stream);
   if (rc != GCA_OK) {
     delete c;
@@ -502,6 +509,32 @@ int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const voi
 int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
              float* lse, void* stream) {
   return step_impl(c, layer, q, k, v, out, lse, -1, stream);
+}
+
+int gca_frame_attention(gca_ctx* c, const void* q, const void* k, const void* v, void* out,
+                        float* lse, int32_t frames, void* stream) {
+  if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  if (!q || !k || !v || !out) return fail(GCA_E_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (frames < 0) return fail(GCA_E_INVALID_ARG, "frames must be >= 0");
+  const Geometry& g = c->g;
+  hipStream_t st = (hipStream_t)stream;
+  // every frame is a lone "appended frame" over the scratch pages 0..ppf-1
+  PageList pl{};
+  pl.s_last_valid = kPage;
+  pl.fresh_cnt = g.ppf;
+  pl.ppf = g.ppf;
+  pl.f_last_valid = g.f_last_valid;
+  FramePages pages{};
+  for (int j = 0; j < g.ppf; ++j) pages.p[j] = j;
+  const size_t rows = (size_t)g.F * c->cfg.num_heads * c->cfg.head_dim;
+  for (int f = 0; f < frames; ++f) {
+    const size_t off = (size_t)f * rows * g.eb;
+    int rc = run_step_kernels(c, 0, (const char*)q + off, (const char*)k + off, (const char*)v + off,
+                              (char*)out + off, lse ? lse + (size_t)f * c->cfg.num_heads * g.F : nullptr,
+                              g.F, pl, pages, -1, nullptr, g.F, st, true);
+    if (rc != GCA_OK) return rc;
+  }
+  return GCA_OK;
 }
 
 int gca_step_keyframe(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v,

@@ -122,6 +122,17 @@ int gca_step(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const vo
 int gca_step_keyframe(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
                       void* out, float* lse, int32_t append, void* stream);
 
+/* Intra-frame attention (the frame-attention layers that alternate with the
+ * GCA layers: technical summary §2.1; news article, pipeline figure): full,
+ * unmasked softmax attention of each frame's M+S tokens among themselves,
+ * for `frames` frames one after the other.  Uses the context's shape, dtype
+ * and scale and a scratch of ceil((M+S)/P) pages inside the workspace; no
+ * layer's cache is read or changed.
+ *   q, k, v: [frames, M+S, H, D] (device);  out: [frames, M+S, H, D] (device);
+ *   lse: [frames, H, M+S] fp32 or NULL. */
+int gca_frame_attention(gca_ctx* ctx, const void* q, const void* k, const void* v, void* out,
+                        float* lse, int32_t frames, void* stream);
+
 /* Free every page of every layer and return all layers to the empty state
  * (window reset of the windowed mode: paper-to-code map §五). */
 int gca_reset(gca_ctx* ctx, void* stream);

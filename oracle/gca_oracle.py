@@ -195,6 +195,23 @@ def anchor_init(q, k, v, scale: float):
     return masked_attention(q, k, v, None, scale)
 
 
+def frame_attention(q, k, v, scale: float):
+    """Intra-frame attention: each frame's F tokens attend to all of themselves.
+
+    The model alternates frame-attention layers with the GCA layers
+    (technical summary §2.1; news article, pipeline figure); a frame-attention
+    layer is plain unmasked softmax attention inside one frame.
+    q, k, v: [B, F, H, D].  Returns O [B, F, H, D] and LSE [B, H, F].
+    """
+    B = q.shape[0]
+    outs, lses = [], []
+    for b in range(B):
+        o, l = masked_attention(q[b], k[b], v[b], None, scale)
+        outs.append(o)
+        lses.append(l)
+    return np.stack(outs), np.stack(lses)
+
+
 def step(t: int, q_t, get_rows, shp: GcaShape, scale: float):
     """GCA output for streaming frame t >= n.
 
