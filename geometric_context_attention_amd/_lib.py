@@ -87,6 +87,7 @@ _SIGS = {
                                       ctypes.POINTER(ctypes.c_size_t)]),
     "gca_step_keyframe": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_frame_attention": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
+    "gca_set_rotary": (ctypes.c_int, [_VP, _VP]),
     "gca_profile_enable": (ctypes.c_int, [_VP, _I32]),
     "gca_profile_read": (ctypes.c_int, [_VP, ctypes.POINTER(gca_profile)]),
 }
@@ -183,6 +184,11 @@ def gca_frame_attention(ctx, q, k, v, out, lse=None, frames=1, stream=None):
     _check(lib().gca_frame_attention(ctx, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
                                      _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
                                      frames, _stream_ptr(stream)))
+
+
+def gca_set_rotary(ctx, cos_sin=None):
+    """cos_sin: device fp32 tensor [rows, D/2, 2] for the following calls, or None."""
+    _check(lib().gca_set_rotary(ctx, _ptr(cos_sin, torch.float32, name="cos_sin")))
 
 
 def gca_reset(ctx, stream=None):

@@ -83,6 +83,10 @@ struct AttnArgs {
   float2* part_ml;      // [H][nsplit][Lq_pad] (max of raw scores, sum of exp)
   int32_t Lq_pad;       // round_up(Lq, 512)
   int32_t pool;         // pages in the pool (entries outside [0, pool) are masked)
+  // rotary position embedding: (cos, sin) of channel pair i of row r at
+  // rope[r * D/2 + i] for the query rows and, with the same row index, the
+  // appended frame's key rows (null: no rotation)
+  const float2* rope;
   // profiling: workgroup 0 adds its duration in shader cycles to clock[0] and
   // in 100 MHz reference ticks to clock[1] (null: not sampled)
   unsigned long long* clock;
@@ -110,7 +114,7 @@ hipError_t launch_reset(const LayerDev& L, int pool_words, int ftab_entries, int
                         hipStream_t st);
 hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int frame,
                          const FramePages& pages, int ppf, int F, int H, bool f32,
-                         hipStream_t st);
+                         const float2* rope, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st);
 // Merge of the key splits (when a.nsplit > 1) and the eviction (when ev != null),
 // in one launch.

@@ -45,6 +45,46 @@ __global__ void k_reset(LayerDev L, int pool_words, int ftab_entries, int slist_
   if (i < kCtrCount) L.ctr[i] = 0;
 }
 
+// Rotary position embedding (RoFormer): channels (2i, 2i+1) of a row turn by
+// the angle whose cosine and sine are given.  Each product and the sum are
+// rounded separately (no fused multiply-add), so the rotated values are the
+// ones an unfused fp32 evaluation of the same formula gives.
+__device__ __forceinline__ void rope_rotate(float& x0, float& x1, float2 cs) {
+#pragma clang fp contract(off)
+  const float y0 = x0 * cs.x - x1 * cs.y;
+  const float y1 = x0 * cs.y + x1 * cs.x;
+  x0 = y0;
+  x1 = y1;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// Stream elements: bf16 bits (uint16_t) or fp32; bf16 rounding is RNE.
+__device__ __forceinline__ float elem_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+__device__ __forceinline__ float elem_to_f32(float x) { return x; }
+template <typename T>
+__device__ __forceinline__ T f32_to_elem(float x);
+template <>
+__device__ __forceinline__ uint16_t f32_to_elem<uint16_t>(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+template <>
+__device__ __forceinline__ float f32_to_elem<float>(float x) { return x; }
+
+// Rotate a 16-byte chunk of 8 bf16 channels d0 .. d0+7 (pairs d0/2 ..) of one row.
+__device__ __forceinline__ uint4 rope_bf16x8(uint4 v, const float2* cs) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+    rope_rotate(x0, x1, cs[e]);
+    w[e] = pack_bf16(x0, x1);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Grid (ppf, H): copy one head's 64 slots of one page of frame `frame` into
 // the page the host chose for it.  K rows are copied as they are; V rows are
 // transposed through LDS.  Slots past the frame's last row are zero-filled.
@@ -53,7 +93,8 @@ __global__ void k_reset(LayerDev L, int pool_words, int ftab_entries, int slist_
 template <typename T>
 __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict__ kin,
                                                 const T* __restrict__ vin, int frame,
-                                                FramePages pages, int ppf, int F, int H) {
+                                                FramePages pages, int ppf, int F, int H,
+                                                const float2* __restrict__ rope) {
   constexpr int D = kHeadDim, P = kPage;
   const int j = blockIdx.x, h = blockIdx.y;
   const int page = pages.p[j];
@@ -72,6 +113,19 @@ __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict_
     }
     kdst[e] = kv;
     tile[s][d] = vv;
+  }
+  if (rope != nullptr) {  // K rows rotated (the frame's rows of the table)
+    __syncthreads();
+    for (int e = threadIdx.x; e < P * D / 2; e += 256) {
+      const int s = e / (D / 2), i = e % (D / 2);
+      if (s < nvalid) {
+        const size_t src = ((size_t)(row0 + s) * H + h) * D + 2 * i;
+        float x0 = elem_to_f32(kin[src]), x1 = elem_to_f32(kin[src + 1]);
+        rope_rotate(x0, x1, rope[(size_t)(row0 + s) * (D / 2) + i]);
+        kdst[s * D + 2 * i] = f32_to_elem<T>(x0);
+        kdst[s * D + 2 * i + 1] = f32_to_elem<T>(x1);
+      }
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < P * D; e += 256) {
@@ -497,8 +551,12 @@ __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing]
 #pragma unroll
     for (int u = 0; u < kFreshBatch; ++u) {
       if (b0 + u < p1) {
-        const int pg = a.fresh.p[b0 + u - f0];
+        const int j = b0 + u - f0;
+        const int pg = a.fresh.p[j];
         const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
+        const int valid = (j == a.pl.ppf - 1) ? a.pl.f_last_valid : kPage;
+        if (a.rope != nullptr && row < valid)  // rotated keys are what the cache holds
+          kv[u] = rope_bf16x8(kv[u], a.rope + (size_t)(j * kPage + row) * (kHeadDim / 2) + ch * 4);
         *reinterpret_cast<uint4*>(kpool + off + row * 64 + ch * 8) = kv[u];
         const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
         // V^T element (d, col) sits at chunk (col >> 3) ^ (d >> 3) of row d:
@@ -573,8 +631,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row < a.Lq)
+      if (row < a.Lq) {
         v = *reinterpret_cast<const uint4*>(qbase + ((size_t)row * H + h) * D + c * 16 + hf * 8);
+        if (a.rope != nullptr) v = rope_bf16x8(v, a.rope + (size_t)row * (D / 2) + c * 8 + hf * 4);
+      }
       qf[j][c] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -721,6 +781,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
     qv[d] = live ? q[((size_t)row * H + h) * D + d] : 0.f;
     o[d] = 0.f;
   }
+  if (live && a.rope != nullptr) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) rope_rotate(qv[2 * i], qv[2 * i + 1], a.rope[(size_t)row * (D / 2) + i]);
+  }
   float m = -INFINITY, l = 0.f;
   const float c2 = a.scale_log2;
   float* kpool = reinterpret_cast<float*>(a.kpool);
@@ -748,6 +812,13 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
         }
         sK[r][d] = kv;
         sV[d][swap23(r)] = vv;
+      }
+      if (a.rope != nullptr) {  // rotated keys are what the cache holds
+        __syncthreads();
+        for (int e = threadIdx.x; e < P * D / 2; e += 256) {
+          const int r = e / (D / 2), i = e % (D / 2);
+          if (r < valid) rope_rotate(sK[r][2 * i], sK[r][2 * i + 1], a.rope[(size_t)(fj * P + r) * (D / 2) + i]);
+        }
       }
     }
     __syncthreads();
@@ -937,14 +1008,14 @@ hipError_t launch_reset(const LayerDev& L, int pool_words, int ftab_entries, int
 
 hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int frame,
                          const FramePages& pages, int ppf, int F, int H, bool f32,
-                         hipStream_t st) {
+                         const float2* rope, hipStream_t st) {
   dim3 grid(ppf, H);
   if (f32)
     hipLaunchKernelGGL(k_append<float>, grid, dim3(256), 0, st, L, (const float*)k,
-                       (const float*)v, frame, pages, ppf, F, H);
+                       (const float*)v, frame, pages, ppf, F, H, rope);
   else
     hipLaunchKernelGGL(k_append<uint16_t>, grid, dim3(256), 0, st, L, (const uint16_t*)k,
-                       (const uint16_t*)v, frame, pages, ppf, F, H);
+                       (const uint16_t*)v, frame, pages, ppf, F, H, rope);
   return hipGetLastError();
 }
 

@@ -223,6 +223,7 @@ struct gca_ctx {
   float2* part_ml = nullptr;
   unsigned long long* clock = nullptr;  // [2] device: shader cycles, reference ticks
   LayerDev scratch{};                   // ppf K/V pages for frame attention (pools only)
+  const float2* rope = nullptr;         // rotary table of the next calls (gca_set_rotary)
   unsigned long long clock_base[2] = {0, 0};
   bool f32 = false;
   // profiling
@@ -284,6 +285,7 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.part_ml = c->part_ml;
   a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
   a.pool = use_scratch ? c->g.ppf : c->g.pool;
+  a.rope = c->rope;
   a.clock = c->prof ? c->clock : nullptr;
   EventPair* ep = nullptr;
   if (c->prof) {
@@ -407,7 +409,8 @@ int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, con
     hs.alloc_frame(f, g.ppf, g.pool, pages);
     hipError_t e = launch_append(c->dev[layer], (const char*)k + f * frame_bytes,
                                  (const char*)v + f * frame_bytes, f, pages, g.ppf, g.F,
-                                 cfg.num_heads, c->f32, st);
+                                 cfg.num_heads, c->f32,
+                                 c->rope ? c->rope + (size_t)f * g.F * (kHeadDim / 2) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "append launch");
   }
   PageList pl{};
@@ -511,6 +514,12 @@ int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void
   return step_impl(c, layer, q, k, v, out, lse, -1, stream);
 }
 
+int gca_set_rotary(gca_ctx* c, const float* cos_sin) {
+  if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  c->rope = reinterpret_cast<const float2*>(cos_sin);
+  return GCA_OK;
+}
+
 int gca_frame_attention(gca_ctx* c, const void* q, const void* k, const void* v, void* out,
                         float* lse, int32_t frames, void* stream) {
   if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
@@ -527,14 +536,17 @@ int gca_frame_attention(gca_ctx* c, const void* q, const void* k, const void* v,
   FramePages pages{};
   for (int j = 0; j < g.ppf; ++j) pages.p[j] = j;
   const size_t rows = (size_t)g.F * c->cfg.num_heads * c->cfg.head_dim;
-  for (int f = 0; f < frames; ++f) {
+  const float2* table = c->rope;
+  int rc = GCA_OK;
+  for (int f = 0; f < frames && rc == GCA_OK; ++f) {
     const size_t off = (size_t)f * rows * g.eb;
-    int rc = run_step_kernels(c, 0, (const char*)q + off, (const char*)k + off, (const char*)v + off,
-                              (char*)out + off, lse ? lse + (size_t)f * c->cfg.num_heads * g.F : nullptr,
-                              g.F, pl, pages, -1, nullptr, g.F, st, true);
-    if (rc != GCA_OK) return rc;
+    if (table != nullptr) c->rope = table + (size_t)f * g.F * (kHeadDim / 2);
+    rc = run_step_kernels(c, 0, (const char*)q + off, (const char*)k + off, (const char*)v + off,
+                          (char*)out + off, lse ? lse + (size_t)f * c->cfg.num_heads * g.F : nullptr,
+                          g.F, pl, pages, -1, nullptr, g.F, st, true);
   }
-  return GCA_OK;
+  c->rope = table;
+  return rc;
 }
 
 int gca_step_keyframe(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v,

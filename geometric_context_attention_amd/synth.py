@@ -75,3 +75,26 @@ def draw_frames(spec: StreamSpec, layer: int, first: int, count: int, device="cp
         hi = min(first + count, (c + 1) * C) - c * C
         qs.append(q[lo:hi]); ks.append(k[lo:hi]); vs.append(v[lo:hi])
     return torch.cat(qs), torch.cat(ks), torch.cat(vs)
+
+
+def rotary_table(first: int, count: int, F: int, S: int, D: int = 64, grid_w: int = 37,
+                 base: float = 10000.0) -> torch.Tensor:
+    """Synthetic rotary angles for frames [first, first+count): fp32 [count, F, D/2, 2].
+
+    The pages fix no frequency schedule, so this stand-in for a video (3-axis)
+    schedule is an input like the others: channel pair i uses axis i % 3
+    (frame time, patch row, patch column) with frequency base^(-(i // 3) / (D/6));
+    summary rows sit at patch (0, 0), image row S + p at patch (p // grid_w,
+    p % grid_w).  Entry [f, r, i] = (cos, sin) of position * frequency.
+    """
+    half = D // 2
+    i = torch.arange(half, dtype=torch.float64)
+    axis = (i % 3).long()
+    freq = base ** (-(torch.div(i, 3, rounding_mode="floor")) / (D / 6))
+    t = torch.arange(first, first + count, dtype=torch.float64)[:, None].expand(count, F)
+    p = torch.clamp(torch.arange(F, dtype=torch.float64) - S, min=-1)
+    y = torch.where(p < 0, torch.zeros_like(p), torch.div(p, grid_w, rounding_mode="floor"))
+    x = torch.where(p < 0, torch.zeros_like(p), p - y * grid_w)
+    pos = torch.stack([t, y[None].expand(count, F), x[None].expand(count, F)], dim=-1)  # [count, F, 3]
+    ang = pos[..., axis] * freq  # [count, F, half]
+    return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).to(torch.float32).contiguous()

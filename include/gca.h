@@ -122,6 +122,19 @@ int gca_step(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const vo
 int gca_step_keyframe(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
                       void* out, float* lse, int32_t append, void* stream);
 
+/* Rotary position embedding for the calls that follow (technical summary
+ * §2.7 and the deep dive's 3D-RoPE switch: the model encodes frame time, and
+ * optionally patch position, into Q and K; the frequency schedule is not on
+ * the pages, so the caller supplies the angles).  cos_sin: device fp32 table
+ * [rows][D/2][2] holding (cos, sin) of the angle by which channels (2i, 2i+1)
+ * of each row turn (RoFormer rotation, each product rounded separately);
+ * rows are the rows of the call: M+S for gca_step / gca_step_keyframe, n*(M+S)
+ * for gca_anchor_init, frames*(M+S) for gca_frame_attention.  Queries are
+ * rotated before attention and keys before they enter the cache (cached keys
+ * stay rotated; V is never rotated).  The table is read when the kernels run,
+ * so it must stay valid until then.  NULL switches rotation off (the default). */
+int gca_set_rotary(gca_ctx* ctx, const float* cos_sin);
+
 /* Intra-frame attention (the frame-attention layers that alternate with the
  * GCA layers: technical summary §2.1; news article, pipeline figure): full,
  * unmasked softmax attention of each frame's M+S tokens among themselves,

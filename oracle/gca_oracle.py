@@ -195,6 +195,27 @@ def anchor_init(q, k, v, scale: float):
     return masked_attention(q, k, v, None, scale)
 
 
+def rotary(x, cos_sin):
+    """Rotary position embedding (RoFormer, Su et al.): channels (2i, 2i+1) of
+    each row turn by the angle whose (cos, sin) the table gives.
+
+    The model encodes frame time (and optionally patch position) this way
+    (technical summary §2.7; deep dive §3.1, the 3D-RoPE switch); the angles
+    are inputs because the pages fix no frequency schedule.
+    x: [rows, H, D]; cos_sin: [rows, D/2, 2].  Returns float64 [rows, H, D].
+    Parity status: pinned against complex multiplication and the rotation
+    group laws in tests/test_rotary.py.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    cs = np.asarray(cos_sin, dtype=np.float64)
+    c, s = cs[:, None, :, 0], cs[:, None, :, 1]
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
 def frame_attention(q, k, v, scale: float):
     """Intra-frame attention: each frame's F tokens attend to all of themselves.
 
