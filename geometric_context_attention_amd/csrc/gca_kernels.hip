@@ -640,6 +640,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   }
 
   const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
+  const int np = p1 - p0;                // >= 1: there are never more splits than pages
   if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
   if (p0 + tid < p1) plist[tid] = page_entry(a, raw0, valid0);
   for (int i = p0 + tid + NW * 64; i < p1; i += NW * 64) {
@@ -648,8 +649,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
     plist[i - p0] = page_entry(a, raw, valid);
   }
   __syncthreads();
-  auto page_id = [&](int i) { return (int)(__builtin_amdgcn_readfirstlane(plist[i - p0]) >> 7); };
-  auto page_valid = [&](int i) { return (int)(__builtin_amdgcn_readfirstlane(plist[i - p0]) & 127u); };
+  // list entry (page id << 7 | valid slots) of split page i, clamped to the
+  // last one (the ring is kept full past the end with copies of that page)
+  auto entry = [&](int i) { return __builtin_amdgcn_readfirstlane(plist[(i < np ? i : np - 1)]); };
 
   f32x16 o[2][NJ];
 #pragma unroll
@@ -678,13 +680,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   // before the next barrier it waits for its part of page j+2: B reads page
   // j+2 two phases after that barrier but A already one phase after it.
   const bool grp_a = GCA_PINGPONG ? wave < 4 : true;
-  const int np = p1 - p0;  // >= 1: there are never more splits than pages
   // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed; a page
   // this workgroup has just written is only staged after its stores completed
   if (a.pl.fresh_cnt > 0 && f0 < p1 && f0 - p0 < kAhead) GCA_WAIT_VMCNT(0);
+  // ent[s]: list entry of the page in ring slot s, kept in scalar registers
+  // from its staging on, so that no phase waits on an LDS read for it
+  uint32_t ent[kRing];
 #pragma unroll
-  for (int u = 0; u < kAhead; ++u) stage_page(a, ring, u, page_id(p0 + u < p1 ? p0 + u : p1 - 1), h, tid);
-  int pg_ahead = page_id(p0 + kAhead < p1 ? p0 + kAhead : p1 - 1);
+  for (int u = 0; u < kAhead; ++u) {
+    ent[u] = entry(u);
+    stage_page(a, ring, u, (int)(ent[u] >> 7), h, tid);
+  }
+  uint32_t ent_ahead = entry(kAhead);
   GCA_WAIT_VMCNT(2 * (kAhead - 2));
   wg_barrier();
   if (!grp_a) wg_barrier();  // group B runs one phase behind
@@ -693,12 +700,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   bf16x8 pf[NJ][4];
   auto page_step = [&](int jj, auto slot_c) {
     constexpr int S = decltype(slot_c)::value;  // ring slot of page p0 + jj
-    const int j = p0 + jj;
+    constexpr int SA = (S + kAhead) % kRing;    // slot page p0 + jj + kAhead goes to
+    // the entry after that one is read before the MFMA phase's own LDS reads,
+    // so it has landed by the time it is used
+    const uint32_t raw_next = plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
     mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], jj > 0, qf, pf, o, sc, l32, hf);
     if (GCA_PINGPONG) wg_barrier();
-    stage_page(a, ring, (S + kAhead) % kRing, pg_ahead, h, tid);
-    pg_ahead = page_id(j + kAhead + 1 < p1 ? j + kAhead + 1 : p1 - 1);
-    valu_phase<NJ>(sc, page_valid(j), m, l, o, pf, c2, hf);
+    ent[SA] = ent_ahead;
+    stage_page(a, ring, SA, (int)(ent_ahead >> 7), h, tid);
+    ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
+    valu_phase<NJ>(sc, (int)(ent[S] & 127u), m, l, o, pf, c2, hf);
     GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
     wg_barrier();
   };
