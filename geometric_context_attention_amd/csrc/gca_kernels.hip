@@ -309,6 +309,7 @@ constexpr int kRing = GCA_RING;    // LDS page slots
 constexpr int kAhead = GCA_AHEAD;  // a wave stages page j + kAhead while it computes page j
 static_assert(kRing >= kAhead + 2, "a slot is refilled only after both wave groups have read it");
 constexpr int kTileElems = 4096;
+constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kAttnWaves = 8;  // 512 threads, 2 waves per SIMD
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -369,21 +370,26 @@ __device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf
     }
 }
 
-// p = exp2((s - m) * scale * log2 e) as packed bf16 P^T fragments
-// (pf[j][kc]: 16-key chunk kc of the page); psum[j] is the sum of the same
-// rounded values over this lane's 32 keys (v_dot2 with (1, 1)).
-template <int NJ>
-__device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float (&m)[NJ],
-                                         bf16x8 (&pf)[NJ][4], float (&psum)[NJ], float c2) {
+// The running max m of a row is kept in log2 units of the scaled scores
+// (s * scale * log2 e).  The MFMA phase turns the scores of a page in place
+// into x = s * scale * log2 e - m, beside the PV product (see mfma_phase);
+// the VALU phase then only exponentiates.
+//
+// p = exp2(x - shift) as packed bf16 P^T fragments (pf[j][kc]: 16-key chunk
+// kc of the page); psum[j] is the sum of the same rounded values over this
+// lane's 32 keys (v_dot2 with (1, 1)).
+template <int NJ, bool kShift>
+__device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float (&shift)[NJ],
+                                         bf16x8 (&pf)[NJ][4], float (&psum)[NJ]) {
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const float mc = m[j] * c2;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        pf[j][kt * 2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][j][r], c2, -mc));
+        pf[j][kt * 2 + (r >> 3)][r & 7] =
+            (__bf16)__builtin_amdgcn_exp2f(kShift ? sc[kt][j][r] - shift[j] : sc[kt][j][r]);
     float acc = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
@@ -396,11 +402,12 @@ __device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float 
   }
 }
 
-// Move the running max to the page's column max where that is larger and
-// rescale l and O by the drop in exp2 units.
+// Move the running max up to the page's row max (on a split's first page:
+// set it, nothing has been summed yet) and rescale l and O by the rise;
+// shift[j] receives the rise, by which the page's x must still come down.
 template <int NJ>
 __device__ __forceinline__ void raise_max(const f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
-                                          f32x16 (&o)[2][NJ], float c2) {
+                                          f32x16 (&o)[2][NJ], float (&shift)[NJ], bool first) {
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const f32x16& u = sc[0][j];
@@ -411,43 +418,42 @@ __device__ __forceinline__ void raise_max(const f32x16 (&sc)[2][NJ], float (&m)[
     const float g = max3f(v[2], v[3], v[4]), h = max3f(v[5], v[6], v[7]);
     const float i = max3f(v[8], v[9], v[10]), k = max3f(v[11], v[12], v[13]);
     const float x = max3f(max3f(a, b, c), max3f(d, e, f), max3f(g, h, i));
+    // finite: every page holds a visible key for every row
     const float mx = half_pair_max(max3f(x, k, fmaxf(v[14], v[15])));
-    const float mnew = fmaxf(m[j], mx);
-    const float alpha = __builtin_amdgcn_exp2f((m[j] - mnew) * c2);  // 0 while m is -inf
-    l[j] *= alpha;
+    shift[j] = first ? mx : fmaxf(mx, 0.f);
+    if (!first) {
+      const float alpha = __builtin_amdgcn_exp2f(-shift[j]);
+      l[j] *= alpha;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      o[0][j][r] *= alpha;
-      o[1][j][r] *= alpha;
+      for (int r = 0; r < 16; ++r) {
+        o[0][j][r] *= alpha;
+        o[1][j][r] *= alpha;
+      }
     }
-    m[j] = mnew;
+    m[j] += shift[j];
   }
 }
 
-// VALU phase of page j: mask its empty slots, turn the scores into P (bf16)
-// against the current running max and add the row sums.  The max is not
-// looked at unless some lane's sum over its 32 keys exceeds 2^kSumLimitLog2
-// (or is inf: the first page, while m is still -inf); only then is it raised
-// to the page max, O and l rescaled and P recomputed.  Every p is therefore
-// at most 2^kSumLimitLog2, far from fp32 overflow in O and l, and since the
-// max only grows from values that occurred, P keeps bf16's relative
-// precision.  Every page holds at least one visible key for every row, so
-// the raised max is finite.
+// VALU phase of page j: turn x into P (bf16) and add the row sums.  The max
+// is not looked at unless some lane's sum over its 32 keys exceeds
+// 2^kSumLimitLog2 (or is inf), or on a split's first page, where it starts
+// from that page's row max; only then is it raised to the page max, O and l
+// rescaled and P recomputed.  Every p is therefore at most 2^kSumLimitLog2,
+// far from fp32 overflow in O and l, and since the max only grows from
+// values that occurred, P keeps bf16's relative precision.
 constexpr uint32_t kSumLimitBits = 0x47800000u;  // 2^16 as fp32 bits; inf and NaN compare above
 
 template <int NJ>
-__device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], int valid, float (&m)[NJ],
-                                           float (&l)[NJ], f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4],
-                                           float c2, int hf) {
-  if (valid < kPage) mask_page<NJ>(sc, valid, hf);
-  float psum[NJ];
-  page_exp<NJ>(sc, m, pf, psum, c2);
-  bool big = false;
+__device__ __forceinline__ void valu_phase(const f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
+                                           f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4], bool first) {
+  float psum[NJ], shift[NJ];
+  page_exp<NJ, false>(sc, shift, pf, psum);
+  bool big = first;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) big |= __builtin_bit_cast(uint32_t, psum[j]) > kSumLimitBits;
   if (__any(big)) {
-    raise_max<NJ>(sc, m, l, o, c2);
-    page_exp<NJ>(sc, m, pf, psum, c2);
+    raise_max<NJ>(sc, m, l, o, shift, first);
+    page_exp<NJ, true>(sc, shift, pf, psum);
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) l[j] += psum[j];
@@ -469,27 +475,15 @@ __device__ __forceinline__ void stage_page(const AttnArgs& a, uint16_t (&ring)[2
   __builtin_amdgcn_global_load_lds(vp, &ring[kRing + slot][wave * 512], 16, 0, 0);
 }
 
-// MFMA phase of page j: PV of page j-1 (P from the previous VALU phase, V^T
-// from slot sv) and QK^T of page j (K from slot sk).
+// MFMA phase of page j: QK^T of page j (K from slot sk), the empty slots of
+// its scores masked, then PV of page j-1 (P from the previous VALU phase, V^T
+// from slot sv) with, beside it, the scores turned in place into
+// x = s * c2 - m (c2 = scale * log2 e): the VALU works while the matrix core
+// does, and its work fills the waits on the V operand reads.
 template <int NJ>
-__device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* sv, bool pv,
-                                           const bf16x8 (&qf)[NJ][4], const bf16x8 (&pf)[NJ][4],
-                                           f32x16 (&o)[2][NJ], f32x16 (&sc)[2][NJ], int l32, int hf) {
-  if (pv) {
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&sv[swz(dt * 32 + l32, kc * 2 + hf)]);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][kc], o[dt][j], 0, 0, 0);
-      }
-    }
-  }
-  // PV and QK^T in program order: interleaving them keeps P, the new scores
-  // and both operand sets live at once, more than 256 registers
-  __builtin_amdgcn_sched_barrier(0);
+__device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* sv, const bf16x8 (&qf)[NJ][4],
+                                           const bf16x8 (&pf)[NJ][4], f32x16 (&o)[2][NJ], f32x16 (&sc)[2][NJ],
+                                           const float (&m)[NJ], float c2, int valid, int l32, int hf) {
   if (sk != nullptr) {
     const f32x16 zero = {};
 #pragma unroll
@@ -503,7 +497,43 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
           sc[kt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[kt][j], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (valid < kPage) mask_page<NJ>(sc, valid, hf);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // PV: V fragment i (kc = i / 2, dt = i % 2) is read two fragments ahead;
+  // after each of its MFMAs come four of the 64 multiply-adds, and a
+  // scheduling fence after each fragment keeps that order
+  auto vfrag = [&](int i) {
+    return *reinterpret_cast<const bf16x8*>(&sv[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+  };
+  bf16x8 vbuf[2] = {vfrag(0), vfrag(1)};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x8 vf = vbuf[i % 2];
+    if (i + 2 < 8) vbuf[i % 2] = vfrag(i + 2);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      o[i % 2][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][i / 2], o[i % 2][j], 0, 0, 0);
+      if (sk != nullptr) {
+        // multiply-adds 4u .. 4u+3 of the 64 (u = 2i + j): tile (u / 8, u / 4 % 2), registers 4(u % 4) ..
+        const int u = 2 * i + j;
+        const int kt = (u >> 3) & 1, jq = (u >> 2) & 1, r0 = (u & 3) * 4;
+#pragma unroll
+        for (int r = r0; r < r0 + 4; ++r) sc[kt][jq][r] = __builtin_fmaf(sc[kt][jq][r], c2, -m[jq]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (sk != nullptr) {
+    // keep the multiply-adds here: without a use the compiler would sink them
+    // into the VALU phase
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(sc[kt][j]));
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Write the appended frame's pages that fall in [p0, p1) to their pool pages:
@@ -660,10 +690,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
-  float m[NJ], l[NJ];
+  float m[NJ], l[NJ];  // running max (log2 units; 0 until a split's first page sets it), row sum
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    m[j] = -INFINITY;
+    m[j] = 0.f;
     l[j] = 0.f;
   }
   const float c2 = a.scale_log2;
@@ -683,6 +713,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed; a page
   // this workgroup has just written is only staged after its stores completed
   if (a.pl.fresh_cnt > 0 && f0 < p1 && f0 - p0 < kAhead) GCA_WAIT_VMCNT(0);
+  // V tile of slot kRing-1 (read by the first page's MFMA phase) to zero; no
+  // copy writes that slot before the first page's VALU phase
+  static_assert(kTileElems * 2 == NW * 64 * 16, "one 16-byte store per thread clears a tile");
+  *reinterpret_cast<uint4*>(&ring[2 * kRing - 1][tid * 8]) = make_uint4(0u, 0u, 0u, 0u);
   // ent[s]: list entry of the page in ring slot s, kept in scalar registers
   // from its staging on, so that no phase waits on an LDS read for it
   uint32_t ent[kRing];
@@ -697,26 +731,35 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
   if (!grp_a) wg_barrier();  // group B runs one phase behind
 
   f32x16 sc[2][NJ];
+  // the MFMA phase of the first page multiplies this zero P with the V tile
+  // of ring slot kRing-1, which the prologue zeroed, so O stays zero
   bf16x8 pf[NJ][4];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
   auto page_step = [&](int jj, auto slot_c) {
     constexpr int S = decltype(slot_c)::value;  // ring slot of page p0 + jj
     constexpr int SA = (S + kAhead) % kRing;    // slot page p0 + jj + kAhead goes to
     // the entry after that one is read before the MFMA phase's own LDS reads,
     // so it has landed by the time it is used
     const uint32_t raw_next = plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
-    mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], jj > 0, qf, pf, o, sc, l32, hf);
+    mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2, (int)(ent[S] & 127u),
+                   l32, hf);
     if (GCA_PINGPONG) wg_barrier();
     ent[SA] = ent_ahead;
     stage_page(a, ring, SA, (int)(ent_ahead >> 7), h, tid);
     ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
-    valu_phase<NJ>(sc, (int)(ent[S] & 127u), m, l, o, pf, c2, hf);
+    valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
     GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
     wg_barrier();
   };
   for (int jj = 0; jj < np; jj += kRing) for_each_slot<0, kRing>(jj, np, page_step);
   // PV of the last page; group A then takes the barrier that group B took
   // first, so both have passed the same number
-  mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], true, qf, pf, o, sc, l32, hf);
+  mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], qf, pf, o, sc, m, c2, kPage, l32, hf);
   if (GCA_PINGPONG && grp_a) wg_barrier();
   GCA_WAIT_VMCNT(0);  // no copy into LDS outlives the workgroup
 
@@ -743,7 +786,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
             w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
             *reinterpret_cast<uint2*>(out + d) = w;
           }
-        if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * a.scale + logf(l[j]);
+        if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * kLn2 + logf(l[j]);
       }
     } else if (row < a.Lq) {
       // split partial: O / l rounded to bf16, with (m, l) in fp32
@@ -910,12 +953,13 @@ __device__ void merge_block(const AttnArgs& a, int h, int rb) {
       acc.w = __builtin_fmaf(w, x.w, acc.w);
     }
   } else {
-    // normalised bf16 partials O_s / l_s: split s weighs 2^((m_s - M) c2) l_s
+    // normalised bf16 partials O_s / l_s with m_s in log2 units: split s
+    // weighs 2^(m_s - M) l_s
     const uint16_t* po = reinterpret_cast<const uint16_t*>(a.part_o) + first;
 #pragma unroll 4
     for (int s = 0; s < ns; ++s) {
       const float2 v = ml[(size_t)s * a.Lq_pad];
-      const float w = exp2f((v.x - M) * c2) * v.y;
+      const float w = exp2f(v.x - M) * v.y;
       L += w;
       const uint2 x = *reinterpret_cast<const uint2*>(po + s * stride);
       acc.x = __builtin_fmaf(w, __builtin_bit_cast(float, x.x << 16), acc.x);
@@ -937,7 +981,7 @@ __device__ void merge_block(const AttnArgs& a, int h, int rb) {
     w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + o) = w;
   }
-  if (d4 == 0 && a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = M * a.scale + logf(L);
+  if (d4 == 0 && a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = M * (kF32 ? a.scale : kLn2) + logf(L);
 }
 
 // Eviction, one workgroup per head: zero the head's slice of a new summary
