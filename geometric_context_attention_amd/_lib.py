@@ -229,8 +229,9 @@ def gca_pool_views(ctx, layer):
     return kp.value, vp.value, nb.value
 
 
-def gca_profile_enable(ctx, on: bool):
-    _check(lib().gca_profile_enable(ctx, 1 if on else 0))
+def gca_profile_enable(ctx, on, every: int = 1):
+    """Time every `every`-th attention launch with HIP events (on=True), or stop (on=False)."""
+    _check(lib().gca_profile_enable(ctx, int(every) if on else 0))
 
 
 def gca_profile_read(ctx) -> dict:

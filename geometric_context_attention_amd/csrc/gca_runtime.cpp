@@ -228,6 +228,8 @@ struct gca_ctx {
   bool f32 = false;
   // profiling
   bool prof = false;
+  int64_t prof_every = 1;  // time every prof_every-th attention launch
+  int64_t prof_count = 0;
   std::vector<EventPair> ev;
   size_t ev_next = 0;
   double attn_ms = 0, attn_flop = 0, attn_bytes = 0;
@@ -286,9 +288,11 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
   a.pool = use_scratch ? c->g.ppf : c->g.pool;
   a.rope = c->rope;
-  a.clock = c->prof ? c->clock : nullptr;
+  // profiling samples every prof_every-th attention launch
+  const bool sample = c->prof && (c->prof_count++ % c->prof_every) == 0;
+  a.clock = sample ? c->clock : nullptr;
   EventPair* ep = nullptr;
-  if (c->prof) {
+  if (sample) {
     ep = &c->ev[c->ev_next];
     c->ev_next = (c->ev_next + 1) % c->ev.size();
     int rc = harvest(c, *ep);
@@ -644,6 +648,7 @@ int gca_pool_views(gca_ctx* c, int32_t layer, void** k_pool, void** v_pool, size
 
 int gca_profile_enable(gca_ctx* c, int32_t on) {
   if (c == nullptr) return fail(GCA_E_INVALID_ARG, "context is NULL");
+  if (on < 0) return fail(GCA_E_INVALID_ARG, "profile sampling interval is negative");
   if (on) {
     if (c->ev.empty()) {
       c->ev.resize(2048);
@@ -661,7 +666,9 @@ int gca_profile_enable(gca_ctx* c, int32_t on) {
     if (r == hipSuccess) r = hipMemcpy(c->clock_base, c->clock, sizeof(c->clock_base), hipMemcpyDeviceToHost);
     if (r != hipSuccess) return hip_fail(r, "reading the clock counters");
   }
-  c->prof = on != 0;
+  c->prof = on > 0;
+  c->prof_every = on > 0 ? on : 1;
+  c->prof_count = 0;
   return GCA_OK;
 }
 

@@ -212,11 +212,16 @@ typedef struct {
                             workgroup per launch samples; 0 if none ran */
 } gca_profile;
 
-/* Enable (1) or disable (0) HIP-event timing of every attention launch of
- * the context; enabling clears the accumulators (and waits for the device). */
+/* HIP-event timing of the context's attention launches: on = N > 0 times
+ * every N-th launch (1: every launch; a larger N keeps the event records from
+ * slowing the stream), 0 disables.  The launches are counted from this call,
+ * the first one is timed; enabling clears the accumulators (and waits for the
+ * device).  The clock counters are sampled on the same launches.  Returns
+ * GCA_E_INVALID_ARG for on < 0. */
 int gca_profile_enable(gca_ctx* ctx, int32_t on);
 
-/* Wait for the timed launches to finish and return the accumulators. */
+/* Wait for the timed launches to finish and return the accumulators (sums
+ * over the sampled launches only). */
 int gca_profile_read(gca_ctx* ctx, gca_profile* out);
 
 #ifdef __cplusplus
