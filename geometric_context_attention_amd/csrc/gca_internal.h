@@ -90,6 +90,10 @@ struct AttnArgs {
   // profiling: workgroup 0 adds its duration in shader cycles to clock[0] and
   // in 100 MHz reference ticks to clock[1] (null: not sampled)
   unsigned long long* clock;
+  // frames of a batched intra-frame launch (grid y; 1 otherwise): frame f
+  // reads and writes the rows, outputs and rotary angles after those of
+  // frame f-1 and uses the ppf scratch pages after its pages (nsplit == 1)
+  int32_t batch;
 };
 
 // Moving frame `frame` (pages `src`) into the trajectory memory: its S

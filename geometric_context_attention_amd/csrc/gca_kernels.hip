@@ -159,6 +159,16 @@ __global__ __launch_bounds__(256) void k_append(LayerDev L, const T* __restrict_
 // do not count against the vector-memory counter the LDS copies are waited on.
 typedef const int32_t __attribute__((address_space(4)))* const_i32p;
 
+// Page ids of the appended frame, read in place from the kernel's argument
+// block (the kernels below take one AttnArgs by value, which sits at the
+// start of that block).  A per-lane index into the by-value copy would make
+// the compiler move the whole argument block to scratch memory.
+__device__ __forceinline__ const_i32p fresh_page_ids() {
+  typedef const char __attribute__((address_space(4)))* const_bytep;
+  const const_bytep kargs = (const_bytep)__builtin_amdgcn_kernarg_segment_ptr();
+  return (const_i32p)(kargs + offsetof(AttnArgs, fresh) + offsetof(FramePages, p));
+}
+
 __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, int& fj) {
   const PageList& pl = a.pl;
   fj = -1;
@@ -177,7 +187,7 @@ __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, in
     i -= pl.w_cnt;
     fj = i;
     valid = (i == pl.ppf - 1) ? pl.f_last_valid : kPage;
-    pg = a.fresh.p[i];
+    pg = fresh_page_ids()[i];
   }
   if ((unsigned)pg >= (unsigned)a.pool) {
     valid = 0;
@@ -187,15 +197,6 @@ __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, in
   return pg;
 }
 
-// Page ids of the appended frame, read in place from the kernel's argument
-// block (the kernels below take one AttnArgs by value, which sits at the
-// start of that block).  A per-lane index into the by-value copy would make
-// the compiler move the whole argument block to scratch memory.
-__device__ __forceinline__ const_i32p fresh_page_ids() {
-  typedef const char __attribute__((address_space(4)))* const_bytep;
-  const const_bytep kargs = (const_bytep)__builtin_amdgcn_kernarg_segment_ptr();
-  return (const_i32p)(kargs + offsetof(AttnArgs, fresh) + offsetof(FramePages, p));
-}
 
 // Where logical page i's physical id comes from, for one lane (i may differ
 // across lanes): the table entry to load (always a valid address) and the
@@ -258,7 +259,7 @@ __device__ __forceinline__ void decode_wg(const AttnArgs& a, int& h, int& qb, in
 __device__ __forceinline__ void record_fresh_frame(const AttnArgs& a) {
   const int ppf = a.pl.ppf;
   if ((int)threadIdx.x < ppf) {
-    const int p = a.fresh.p[threadIdx.x];
+    const int p = fresh_page_ids()[threadIdx.x];
     a.L.ftab[a.fresh_frame * ppf + threadIdx.x] = p;
     atomicOr(&a.L.bitmap[p >> 5], 1u << (p & 31));
   }
@@ -550,7 +551,7 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
 // a written page is staged before the loop's first wait.
 constexpr int kFreshBatch = 8;
 
-__device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems], int p0,
+__device__ __forceinline__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems], int p0,
                                   int p1, int h, int tid) {
   static_assert(2 * kRing >= kFreshBatch, "one LDS tile per page of a round");
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
@@ -582,7 +583,7 @@ __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing]
     for (int u = 0; u < kFreshBatch; ++u) {
       if (b0 + u < p1) {
         const int j = b0 + u - f0;
-        const int pg = a.fresh.p[j];
+        const int pg = fresh_page_ids()[j];
         const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
         const int valid = (j == a.pl.ppf - 1) ? a.pl.f_last_valid : kPage;
         if (a.rope != nullptr && row < valid)  // rotated keys are what the cache holds
@@ -601,7 +602,7 @@ __device__ void write_fresh_pages(const AttnArgs& a, uint16_t (&ring)[2 * kRing]
 #pragma unroll
     for (int u = 0; u < kFreshBatch; ++u) {
       if (b0 + u < p1) {
-        const int pg = a.fresh.p[b0 + u - f0];
+        const int pg = fresh_page_ids()[b0 + u - f0];
         const size_t off = ((size_t)pg * H + h) * (kPage * kHeadDim);
         *reinterpret_cast<uint4*>(vpool + off + row * 64 + ch * 8) =
             *reinterpret_cast<const uint4*>(&ring[u][row * 64 + ((ch ^ (row >> 3)) << 3)]);
@@ -621,8 +622,29 @@ __device__ __forceinline__ void for_each_slot(int jj, int np, F& f) {
   }
 }
 
+// Arguments of frame blockIdx.y of a batched intra-frame launch: its rows,
+// outputs, rotary angles and scratch pages follow those of the frames before
+// it (identity for blockIdx.y == 0, i.e. every unbatched launch).
+template <int kElemBytes>
+__device__ __forceinline__ AttnArgs batch_frame(const AttnArgs& in) {
+  AttnArgs a = in;
+  const size_t f = blockIdx.y;
+  const size_t rows = (size_t)in.Lq * in.H * kHeadDim * kElemBytes;
+  const size_t pages = (size_t)in.pl.ppf * in.H * kPage * kHeadDim * kElemBytes;
+  a.q = static_cast<const char*>(in.q) + f * rows;
+  a.k_in = static_cast<const char*>(in.k_in) + f * rows;
+  a.v_in = static_cast<const char*>(in.v_in) + f * rows;
+  a.out = static_cast<char*>(in.out) + f * rows;
+  a.kpool = static_cast<char*>(in.kpool) + f * pages;
+  a.vpool = static_cast<char*>(in.vpool) + f * pages;
+  if (in.lse != nullptr) a.lse = in.lse + f * in.H * in.Lq;
+  if (in.rope != nullptr) a.rope = in.rope + f * in.Lq * (kHeadDim / 2);
+  return a;
+}
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
+  const AttnArgs a = batch_frame<2>(a_in);
   static_assert(NW == 8, "the staging layout assumes 512 threads");
   constexpr int NJ = 2;
   constexpr int D = kHeadDim;
@@ -807,7 +829,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
       if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
     }
   }
-  if (a.clock != nullptr && blockIdx.x == 0 && tid == 0) {
+  if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
   }
@@ -815,7 +837,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a) {
 
 // fp32 attention: one thread per query row (256-row blocks).  Each page is
 // staged in LDS; keys are taken one at a time with an online softmax.
-__global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a_in) {
+  const AttnArgs a = batch_frame<4>(a_in);
   constexpr int D = kHeadDim, P = kPage;
   __shared__ float sK[P][D + 1];
   __shared__ float sV[D][P + 1];
@@ -1076,14 +1099,16 @@ hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int fr
 
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   const int grid = a.H * a.qblocks * a.nsplit;
+  if (a.batch < 1 || (a.batch > 1 && (a.nsplit != 1 || a.pl.fresh_cnt != a.pl.ppf))) return hipErrorInvalidValue;
+  const dim3 g3(grid, a.batch);
   // the bf16 kernel keeps its split's page list in LDS (the split count is
   // chosen so it always fits; checked here before anything is launched)
   for (int sp = 0; !f32 && sp < a.nsplit; ++sp)
     if (split_begin(a, sp + 1) - split_begin(a, sp) > kListCap) return hipErrorInvalidValue;
   if (f32)
-    hipLaunchKernelGGL(k_attn_f32, dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_attn_f32, g3, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, dim3(grid), dim3(kAttnWaves * 64), 0, st, a);
+    hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, g3, dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ struct Geometry {
   size_t pool_bytes = 0;  // one pool (K or V) of one layer
   size_t meta_bytes = 0;  // bitmap + ftab + slist + ctr of one layer
   size_t part_o_bytes = 0, part_ml_bytes = 0;
-  size_t scratch_bytes = 0;  // one pool (K or V) of ppf pages for frame attention
+  size_t scratch_bytes = 0;  // one pool (K or V) of fa_batch * ppf pages for frame attention
+  int fa_batch = 1;          // frames per batched intra-frame attention launch
   size_t layer_stride = 0;
   size_t total = 0;
   float scale = 0.f;
@@ -152,7 +153,11 @@ void make_geometry(const gca_config& c, Geometry& g) {
   }
   g.part_o_bytes = align256(po);
   g.part_ml_bytes = align256(pml);
-  g.scratch_bytes = align256((size_t)g.ppf * page_bytes);
+  // a batched intra-frame launch fills the CUs with head x query-block x frame
+  // workgroups; each frame of it needs its own ppf scratch pages
+  g.fa_batch = (int)std::min<int64_t>(64, std::max<int64_t>(1, cdiv(kTargetWgs, (int64_t)c.num_heads *
+                                                                                   cdiv(g.F, query_rows(c)))));
+  g.scratch_bytes = align256((size_t)g.fa_batch * g.ppf * page_bytes);
   g.total = g.layer_stride * c.num_layers + g.part_o_bytes + g.part_ml_bytes + kClockBytes +
             2 * g.scratch_bytes;
   g.scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)c.head_dim);
@@ -259,7 +264,7 @@ int harvest(gca_ctx* c, EventPair& e) {
 int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const void* v,
                      void* out, float* lse, int Lq, const PageList& pl, const FramePages& fresh,
                      int fresh_frame, const EvictPlan* ev, int64_t keys, hipStream_t st,
-                     bool use_scratch = false) {
+                     bool use_scratch = false, int batch = 1) {
   const gca_config& cfg = c->cfg;
   AttnArgs a{};
   a.q = q;
@@ -278,7 +283,9 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.F = c->g.F;
   a.qblocks = (int)cdiv(Lq, query_rows(cfg));
   const int64_t npg = (int64_t)pl.a_cnt + pl.s_cnt + pl.w_cnt + pl.fresh_cnt;
-  a.nsplit = choose_splits(cfg, a.qblocks, npg);
+  // a batched launch (intra-frame attention) runs one split per frame
+  a.nsplit = batch > 1 ? 1 : choose_splits(cfg, a.qblocks, npg);
+  a.batch = batch;
   a.scale = c->g.scale;
   a.scale_log2 = (float)(c->g.scale * 1.4426950408889634);
   a.out = out;
@@ -305,8 +312,8 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   if (ep != nullptr) {
     hipError_t r = hipEventRecord(ep->b, st);
     if (r != hipSuccess) return hip_fail(r, "hipEventRecord");
-    ep->flop = 4.0 * Lq * (double)keys * cfg.head_dim * cfg.num_heads;
-    ep->bytes = 2.0 * (double)keys * cfg.num_heads * cfg.head_dim * c->g.eb;
+    ep->flop = 4.0 * Lq * (double)keys * cfg.head_dim * cfg.num_heads * batch;
+    ep->bytes = 2.0 * (double)keys * cfg.num_heads * cfg.head_dim * c->g.eb * batch;
     ep->pending = true;
   }
   e = launch_merge_evict(a, ev, c->f32, st);
@@ -542,12 +549,17 @@ int gca_frame_attention(gca_ctx* c, const void* q, const void* k, const void* v,
   const size_t rows = (size_t)g.F * c->cfg.num_heads * c->cfg.head_dim;
   const float2* table = c->rope;
   int rc = GCA_OK;
-  for (int f = 0; f < frames && rc == GCA_OK; ++f) {
+  // several frames: batches of up to fa_batch frames, one launch each (frame f
+  // of a batch on grid row f, over its own scratch pages); a lone frame: the
+  // split-K path over ppf pages
+  for (int f = 0; f < frames && rc == GCA_OK;) {
+    const int nb = std::min(g.fa_batch, frames - f);
     const size_t off = (size_t)f * rows * g.eb;
     if (table != nullptr) c->rope = table + (size_t)f * g.F * (kHeadDim / 2);
     rc = run_step_kernels(c, 0, (const char*)q + off, (const char*)k + off, (const char*)v + off,
                           (char*)out + off, lse ? lse + (size_t)f * c->cfg.num_heads * g.F : nullptr,
-                          g.F, pl, pages, -1, nullptr, g.F, st, true);
+                          g.F, pl, pages, -1, nullptr, g.F, st, true, nb);
+    f += nb;
   }
   c->rope = table;
   return rc;

@@ -2,7 +2,9 @@
 
 Frames of the stream shapes (M = 500 and a ragged M), bf16 and fp32, are
 attended within themselves through the C ABI and compared with the fp64
-oracle; the call must leave every layer's cache untouched, so a stream
+oracle: a lone frame (the split-K path), and batches below, at and above the
+frames one batched launch takes (16 at H = 16 in bf16, 64 at H = 4 in fp32),
+so the last batch is a partial one; the call must leave every layer's cache untouched, so a stream
 interleaving frame attention with GCA steps still matches the oracle and its
 page state stays bit-exact.
 """
@@ -23,7 +25,8 @@ pytestmark = pytest.mark.gpu
 DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 
-@pytest.mark.parametrize("mode,M,H,B", [("bf16", 500, 16, 3), ("bf16", 181, 4, 5), ("fp32", 58, 2, 4)])
+@pytest.mark.parametrize("mode,M,H,B", [("bf16", 500, 16, 3), ("bf16", 181, 4, 5), ("fp32", 58, 2, 4),
+                                         ("bf16", 500, 16, 1), ("bf16", 500, 16, 21), ("fp32", 120, 4, 70)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6
