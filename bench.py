@@ -12,11 +12,17 @@ layer draws a pool of 64 distinct frames and frame t uses entry
 
 The JSON line also carries:
 * roofline: the attention kernel (the dominant one) against the dense bf16
-  MFMA peak, from HIP events around every attention launch of the timed
+  MFMA peak, from HIP events around every 13th attention launch of the timed
   region (algorithmic flop 4 * (M+6) * keys * D * H per launch);
 * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of the same
   workload (one layer, a few sampled steps, linear in the key count) and
   extrapolated to the whole stream.
+
+Non-default workloads (each prints its own line, without cpu_baseline):
+--keyframe-interval m (frames between keyframes), --summary-tokens S,
+--rotary (rotary angles applied to Q and to K as it is cached), and
+--workload frame-attention (the intra-frame layers through
+gca_frame_attention, --frames-per-call frames per call).
 """
 from __future__ import annotations
 
@@ -52,7 +58,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (x4) for counter calibration")
+    # variants of the stream and the intra-frame layer (not the default line)
+    ap.add_argument("--workload", choices=["stream", "frame-attention"], default="stream")
+    ap.add_argument("--keyframe-interval", type=int, default=1)
+    ap.add_argument("--summary-tokens", type=int, default=6)
+    ap.add_argument("--rotary", action="store_true", help="rotary angles on Q and cached K")
+    ap.add_argument("--frames-per-call", type=int, default=16,
+                    help="frames per gca_frame_attention call (frame-attention workload)")
     return ap.parse_args()
+
+
+def default_workload(args):
+    return (args.workload == "stream" and args.keyframe_interval == 1 and args.summary_tokens == 6
+            and not args.rotary)
 
 
 def copy_calibration(mib):
@@ -95,11 +113,14 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    H, D, M, S, n = 16, 64, args.image_tokens, 6, 3
+    H, D, M, S, n = 16, 64, args.image_tokens, args.summary_tokens, 3
     k, T, Ly = args.window, args.frames, args.layers
     F = M + S
     cfg = G.make_config(num_layers=Ly, num_heads=H, head_dim=D, image_tokens=M, summary_tokens=S,
-                        n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_BF16)
+                        n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_BF16,
+                        keyframe_interval=args.keyframe_interval)
+    if args.workload == "frame-attention":
+        return frame_attention_bench(args, cfg, G, torch, dev)
     stack = G.GcaStack(cfg, device=dev)
     L = G.lib()
     ctx = stack.ctx
@@ -123,6 +144,15 @@ def main():
         ptrs.append([(ctypes.c_void_p(q.data_ptr() + i * fb), ctypes.c_void_p(kk.data_ptr() + i * fb),
                       ctypes.c_void_p(v.data_ptr() + i * fb)) for i in range(R)])
     optr = [ctypes.c_void_p(o.data_ptr()) for o in outs]
+    # rotary angles: a resident table per pool entry (the rotation costs the
+    # same whatever the angles) and one for the anchor block
+    rot_set = L.gca_set_rotary
+    if args.rotary:
+        from geometric_context_attention_amd.synth import rotary_table
+        tabs = rotary_table(0, R, F, S, D).to(dev)
+        tab_anchor = rotary_table(0, n, F, S, D).to(dev).reshape(n * F, D // 2, 2).contiguous()
+        tptr = [ctypes.c_void_p(tabs[i].data_ptr()) for i in range(R)]
+        aptr = ctypes.c_void_p(tab_anchor.data_ptr())
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -135,13 +165,18 @@ def main():
             raise G.GcaError(rc, L.gca_last_error().decode())
         for layer in range(Ly):
             q, kk, v = pools[layer]
+            if args.rotary:
+                rot_set(ctx, aptr)
             rc = anchor_fn(ctx, layer, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kk.data_ptr()),
                            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(anc_out.data_ptr()), None, sp)
             if rc:
                 raise G.GcaError(rc, L.gca_last_error().decode())
         for t in range(n, T):
             for layer in range(Ly):
-                qp, kp, vp = ptrs[layer][(t + 17 * layer) % R]
+                e = (t + 17 * layer) % R
+                qp, kp, vp = ptrs[layer][e]
+                if args.rotary:
+                    rot_set(ctx, tptr[e])
                 rc = step_fn(ctx, layer, qp, kp, vp, optr[layer], None, sp)
                 if rc:
                     raise G.GcaError(rc, L.gca_last_error().decode())
@@ -175,8 +210,11 @@ def main():
         f"{achieved:.1f} TFLOP/s; attention share of wall {attn_avg_ms * timed_launches / 1e3 / elapsed:.2%}; "
         f"shader clock {clock:.2f} GHz")
 
+    variant = [f"keyframe interval {args.keyframe_interval}"] if args.keyframe_interval != 1 else []
+    variant += [f"S={S}"] if S != 6 else []
+    variant += ["rotary Q/K"] if args.rotary else []
     result = {
-        "metric": METRIC,
+        "metric": METRIC if default_workload(args) else f"GCA frames/s ({', '.join(variant)})",
         "value": round(fps, 2),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -189,7 +227,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), resident pool of 64 frames per layer)",
         "config": {"workload": f"GCA direct-mode stream: {Ly} layers, H={H}, D={D}, M={M}+{S}, "
-                               f"n={n}, k={k}, T={T}, keyframe interval 1, bf16",
+                               f"n={n}, k={k}, T={T}, keyframe interval {args.keyframe_interval}, bf16"
+                               + (", rotary Q/K" if args.rotary else ""),
                    "layers": Ly, "heads": H, "head_dim": D, "image_tokens": M,
                    "summary_tokens": S, "n_anchor": n, "k_window": k, "frames": T},
         "roofline": {
@@ -199,7 +238,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": read_traffic() if (T, Ly, k, M) == (10000, 12, 64, 500) else None,
+            "traffic": read_traffic() if (T, Ly, k, M) == (10000, 12, 64, 500) and default_workload(args) else None,
             "avg_launch_us": round(attn_avg_ms * 1e3, 2),
             "launches": timed_launches,
             "sampled_launches": prof["attn_launches"],
@@ -215,8 +254,93 @@ def main():
     del pools
     torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and default_workload(args):
         result["cpu_baseline"] = cpu_baseline(args, H, D, M, S, n, k, T, Ly)
+    print(json.dumps(result), flush=True)
+
+
+def frame_attention_bench(args, cfg, G, torch, dev):
+    """The intra-frame layers: every frame's M+S tokens attend among
+    themselves, in each of the layers, gca_frame_attention taking
+    --frames-per-call frames per call (1 = streaming, one frame per step)."""
+    from geometric_context_attention_amd.synth import StreamSpec, draw_frames
+
+    H, D, M, S, Ly, T = cfg.num_heads, cfg.head_dim, cfg.image_tokens, cfg.summary_tokens, cfg.num_layers, args.frames
+    F = M + S
+    B = args.frames_per_call
+    stack = G.GcaStack(cfg, device=dev)
+    L = G.lib()
+    ctx = stack.ctx
+    R = max(args.pool, B)
+    pools = []
+    for layer in range(Ly):
+        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=32)
+        pools.append(draw_frames(spec, layer, 0, R, device=dev))
+    out = torch.empty((B, F, H, D), dtype=torch.bfloat16, device=dev)
+    fb = F * H * D * 2
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    fa = L.gca_frame_attention
+    calls = [(t, min(B, T - t)) for t in range(0, T, B)]
+
+    def run():
+        for t, nb in calls:
+            for layer in range(Ly):
+                q, kk, v = pools[layer]
+                e = (t + 17 * layer) % (R - nb + 1)  # nb consecutive resident frames
+                rc = fa(ctx, ctypes.c_void_p(q.data_ptr() + e * fb), ctypes.c_void_p(kk.data_ptr() + e * fb),
+                        ctypes.c_void_p(v.data_ptr() + e * fb), ctypes.c_void_p(out.data_ptr()), None, nb, sp)
+                if rc:
+                    raise G.GcaError(rc, L.gca_last_error().decode())
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    G.gca_profile_enable(ctx, True, every=PROFILE_EVERY)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = G.gca_profile_read(ctx)
+    G.gca_profile_enable(ctx, False)
+    fps = args.steps * T / elapsed
+    achieved = prof["attn_flop"] / (prof["attn_ms"] * 1e-3) / 1e12 if prof["attn_ms"] > 0 else 0.0
+    avg_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
+    clock = prof["attn_clock_ghz"]
+    log(f"{fps:.1f} frames/s; attention {prof['attn_launches']} sampled launches, avg {avg_ms * 1e3:.1f} us, "
+        f"{achieved:.1f} TFLOP/s; shader clock {clock:.2f} GHz")
+    result = {
+        "metric": "intra-frame attention frames/s (12 layers, M=500+6, H=16) + % of bf16 MFMA peak",
+        "value": round(fps, 2),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), resident pool of frames per layer)",
+        "config": {"workload": f"intra-frame attention: {Ly} layers, H={H}, D={D}, M={M}+{S}, T={T} frames, "
+                               f"{B} frames per call, bf16", "frames_per_call": B},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "k_attn_bf16",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(avg_ms * 1e3, 2),
+            "sampled_launches": prof["attn_launches"],
+            "algorithmic_flop_per_launch": prof["attn_flop"] / max(prof["attn_launches"], 1),
+            "clock_ghz": round(clock, 3),
+            "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
+        },
+    }
+    stack.close()
     print(json.dumps(result), flush=True)
 
 

@@ -15,6 +15,11 @@ constexpr int kTargetWgs = 256;  // one workgroup per MI355X compute unit
 // resolves its split's page ids into an LDS list of this many entries.
 constexpr int kListCap = 4096;
 constexpr int kMaxFramePages = 32;  // pages of one frame passed by value (F <= 2048)
+// Intra-frame attention of a frame of at most kFrameTiles pages runs in a
+// kernel that holds the whole frame's K and V^T tiles in LDS, up to
+// kFrameBatchMax frames per launch.
+constexpr int kFrameTiles = 8;
+constexpr int kFrameBatchMax = 64;
 
 // Device-side state of one layer's cache, carved from the workspace.
 struct LayerDev {

@@ -622,6 +622,81 @@ __device__ __forceinline__ void for_each_slot(int jj, int np, F& f) {
   }
 }
 
+// Q^T fragments of a bf16 attention workgroup: tile j, d-chunk c: column
+// q = 32j + l32, d = 16c + 8hf .. +7 (rotated when rotary angles are given).
+template <int NJ>
+__device__ __forceinline__ void load_q(const AttnArgs& a, bf16x8 (&qf)[NJ][4], int h, int qb, int wave, int l32,
+                                       int hf) {
+  constexpr int D = kHeadDim;
+  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < a.Lq) {
+        v = *reinterpret_cast<const uint4*>(qbase + ((size_t)row * a.H + h) * D + c * 16 + hf * 8);
+        if (a.rope != nullptr) v = rope_bf16x8(v, a.rope + (size_t)row * (D / 2) + c * 8 + hf * 4);
+      }
+      qf[j][c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+}
+
+// Outputs of a bf16 attention workgroup: with one split, O / l rounded to
+// bf16 and the LSE (natural log); otherwise the split's partial, O / l
+// rounded to bf16 with (m, l) in fp32 (m in log2 units).
+template <int NJ>
+__device__ __forceinline__ void attn_epilogue(const AttnArgs& a, const f32x16 (&o)[2][NJ], const float (&m)[NJ],
+                                              float (&l)[NJ], int h, int qb, int s, int wave, int l32, int hf) {
+  constexpr int D = kHeadDim;
+  const int H = a.H;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) l[j] = half_pair_sum(l[j]);
+  const bool final_out = a.nsplit == 1;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
+    if (final_out) {
+      if (row < a.Lq) {
+        const float inv = 1.f / l[j];
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * H + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = dt * 32 + 8 * g + 4 * hf;
+            __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
+            __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
+            uint2 w;
+            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
+            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
+            *reinterpret_cast<uint2*>(out + d) = w;
+          }
+        if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * kLn2 + logf(l[j]);
+      }
+    } else if (row < a.Lq) {
+      // split partial: O / l rounded to bf16, with (m, l) in fp32
+      const float inv = 1.f / l[j];
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = dt * 32 + 8 * g + 4 * hf;
+          __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
+          __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
+          uint2 w;
+          w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
+          w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
+          *reinterpret_cast<uint2*>(po + d) = w;
+        }
+      if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
+    }
+  }
+}
+
 // Arguments of frame blockIdx.y of a batched intra-frame launch: its rows,
 // outputs, rotary angles and scratch pages follow those of the frames before
 // it (identity for blockIdx.y == 0, i.e. every unbatched launch).
@@ -674,22 +749,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   int valid0;
   const int raw0 = *page_source(a, p0 + tid < p1 ? p0 + tid : p1 - 1, valid0);
 
-  // Q^T fragments: tile j, d-chunk c: column q = 32j + l32, d = 16c + 8hf .. +7
   bf16x8 qf[NJ][4];
-  const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row < a.Lq) {
-        v = *reinterpret_cast<const uint4*>(qbase + ((size_t)row * H + h) * D + c * 16 + hf * 8);
-        if (a.rope != nullptr) v = rope_bf16x8(v, a.rope + (size_t)row * (D / 2) + c * 8 + hf * 4);
-      }
-      qf[j][c] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+  load_q<NJ>(a, qf, h, qb, wave, l32, hf);
 
   const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
   const int np = p1 - p0;                // >= 1: there are never more splits than pages
@@ -785,50 +846,109 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   if (GCA_PINGPONG && grp_a) wg_barrier();
   GCA_WAIT_VMCNT(0);  // no copy into LDS outlives the workgroup
 
-  // epilogue
+  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf);
+  if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
+    atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
+  }
+}
+
+// Intra-frame attention of one (frame, head) per workgroup, the frame at
+// most kFrameTiles pages long: the frame's K tiles and V^T tiles are built
+// once in LDS from the input rows (rotated keys when rotary angles are
+// given), so the page loop reads no memory.  The loop is the ping-pong of the
+// stream kernel without the copies; one split, final outputs.
+
+__global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_in) {
+  const AttnArgs a = batch_frame<2>(a_in);
+  constexpr int NJ = 2;
+  // tiles 0 .. ppf-1: K; kFrameTiles .. kFrameTiles+ppf-1: V^T; the last: zero
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kFrameTiles + 1][kTileElems];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hf = lane >> 5, l32 = lane & 31;
+  int h, qb, s;
+  decode_wg(a, h, qb, s);
+  const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
+  const int ppf = a.pl.ppf;  // <= kFrameTiles (checked at launch)
+  bf16x8 qf[NJ][4];
+  load_q<NJ>(a, qf, h, qb, wave, l32, hf);
+
+  // K row r, chunk c of page j at swz(r, c) of tile j; V^T element (d, col)
+  // (col = swap23(slot), as in the pool) at swz(d, col / 8) + col % 8 of tile
+  // kFrameTiles + j; empty slots are zero
+  {
+    const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
+    const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
+    const int row = tid >> 3, ch = tid & 7;  // one 16-byte chunk of a 64x64 tile per thread
+    const int col = swap23(row);
+    uint4 kv[kFrameTiles], vv[kFrameTiles];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) l[j] = half_pair_sum(l[j]);
-  const bool final_out = a.nsplit == 1;
+    for (int j = 0; j < kFrameTiles; ++j) {
+      const int valid = (j == ppf - 1) ? a.pl.f_last_valid : kPage;
+      kv[j] = make_uint4(0u, 0u, 0u, 0u);
+      vv[j] = kv[j];
+      if (j < ppf && row < valid) {
+        const size_t src = ((size_t)(j * kPage + row) * a.H + h) * kHeadDim + ch * 8;
+        kv[j] = *reinterpret_cast<const uint4*>(kin + src);
+        vv[j] = *reinterpret_cast<const uint4*>(vin + src);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFrameTiles; ++j) {
+      if (j < ppf) {
+        const int valid = (j == ppf - 1) ? a.pl.f_last_valid : kPage;
+        if (a.rope != nullptr && row < valid)
+          kv[j] = rope_bf16x8(kv[j], a.rope + (size_t)(j * kPage + row) * (kHeadDim / 2) + ch * 4);
+        *reinterpret_cast<uint4*>(&lds[j][swz(row, ch)]) = kv[j];
+        const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = ch * 8 + e;
+          lds[kFrameTiles + j][swz(d, col >> 3) + (col & 7)] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+        }
+      }
+    }
+    static_assert(kTileElems * 2 == kAttnWaves * 64 * 16, "one 16-byte store per thread clears a tile");
+    *reinterpret_cast<uint4*>(&lds[2 * kFrameTiles][tid * 8]) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+
+  f32x16 o[2][NJ];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
+  float m[NJ], l[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
-    if (final_out) {
-      if (row < a.Lq) {
-        const float inv = 1.f / l[j];
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * H + h) * D;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = dt * 32 + 8 * g + 4 * hf;
-            __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
-            __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
-            uint2 w;
-            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
-            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
-            *reinterpret_cast<uint2*>(out + d) = w;
-          }
-        if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * kLn2 + logf(l[j]);
-      }
-    } else if (row < a.Lq) {
-      // split partial: O / l rounded to bf16, with (m, l) in fp32
-      const float inv = 1.f / l[j];
-      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = dt * 32 + 8 * g + 4 * hf;
-          __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
-          __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
-          uint2 w;
-          w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
-          w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
-          *reinterpret_cast<uint2*>(po + d) = w;
-        }
-      if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
-    }
+    m[j] = 0.f;
+    l[j] = 0.f;
   }
+  const float c2 = a.scale_log2;
+  f32x16 sc[2][NJ];
+  bf16x8 pf[NJ][4];  // zero P meets the zero V tile on the first page
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
+  const bool grp_a = wave < 4;  // ping-pong as in k_attn_bf16
+  if (!grp_a) wg_barrier();
+  for (int jj = 0; jj < ppf; ++jj) {
+    const int valid = (jj == ppf - 1) ? a.pl.f_last_valid : kPage;
+    mfma_phase<NJ>(lds[jj], lds[jj == 0 ? 2 * kFrameTiles : kFrameTiles + jj - 1], qf, pf, o, sc, m, c2, valid,
+                   l32, hf);
+    wg_barrier();
+    valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
+    wg_barrier();
+  }
+  mfma_phase<NJ>(nullptr, lds[kFrameTiles + ppf - 1], qf, pf, o, sc, m, c2, kPage, l32, hf);
+  if (grp_a) wg_barrier();
+
+  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf);
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
@@ -1105,8 +1225,14 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   // chosen so it always fits; checked here before anything is launched)
   for (int sp = 0; !f32 && sp < a.nsplit; ++sp)
     if (split_begin(a, sp + 1) - split_begin(a, sp) > kListCap) return hipErrorInvalidValue;
+  // intra-frame attention (every page fresh, one split, no cache bookkeeping)
+  // of a frame that fits the LDS tiles: the LDS-resident frame kernel
+  const bool frame = a.pl.a_cnt == 0 && a.pl.s_cnt == 0 && a.pl.w_cnt == 0 && a.fresh_frame < 0 &&
+                     a.nsplit == 1 && a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F;
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, g3, dim3(256), 0, st, a);
+  else if (frame)
+    hipLaunchKernelGGL(k_frame_attn_bf16, g3, dim3(kAttnWaves * 64), 0, st, a);
   else
     hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, g3, dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
