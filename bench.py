@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--keyframe-interval", type=int, default=1)
     ap.add_argument("--summary-tokens", type=int, default=6)
     ap.add_argument("--rotary", action="store_true", help="rotary angles on Q and cached K")
+    ap.add_argument("--reset-every", type=int, default=0, metavar="R",
+                    help="windows of R frames: reset and anchor init at the start of each")
     ap.add_argument("--frames-per-call", type=int, default=16,
                     help="frames per gca_frame_attention call (frame-attention workload)")
     return ap.parse_args()
@@ -70,7 +72,8 @@ def parse():
 
 def default_workload(args):
     return (args.workload == "stream" and args.keyframe_interval == 1 and args.summary_tokens == 6
-            and not args.rotary)
+            and not args.rotary and args.reset_every == 0 and args.layers == 12 and args.window == 64
+            and args.frames == 10000 and args.image_tokens == 500)
 
 
 def copy_calibration(mib):
@@ -116,8 +119,12 @@ def main():
     H, D, M, S, n = 16, 64, args.image_tokens, args.summary_tokens, 3
     k, T, Ly = args.window, args.frames, args.layers
     F = M + S
+    W = args.reset_every if args.reset_every > 0 else T  # frames per window (state reset between)
+    if W <= n or 0 < T % W <= n:
+        print("--reset-every: every window must hold more than the 3 anchor frames", file=sys.stderr)
+        sys.exit(2)
     cfg = G.make_config(num_layers=Ly, num_heads=H, head_dim=D, image_tokens=M, summary_tokens=S,
-                        n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_BF16,
+                        n_anchor=n, k_window=k, max_frames=W, dtype=G.GCA_BF16,
                         keyframe_interval=args.keyframe_interval)
     if args.workload == "frame-attention":
         return frame_attention_bench(args, cfg, G, torch, dev)
@@ -160,6 +167,10 @@ def main():
     anchor_fn = L.gca_anchor_init
 
     def run_stream():
+        for w0 in range(0, T, W):
+            run_window(w0)
+
+    def run_window(w0):
         rc = L.gca_reset(ctx, sp)
         if rc:
             raise G.GcaError(rc, L.gca_last_error().decode())
@@ -171,7 +182,7 @@ def main():
                            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(anc_out.data_ptr()), None, sp)
             if rc:
                 raise G.GcaError(rc, L.gca_last_error().decode())
-        for t in range(n, T):
+        for t in range(w0 + n, min(w0 + W, T)):
             for layer in range(Ly):
                 e = (t + 17 * layer) % R
                 qp, kp, vp = ptrs[layer][e]
@@ -203,7 +214,8 @@ def main():
     frames = args.steps * T
     fps = frames / elapsed
     attn_avg_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
-    timed_launches = args.steps * Ly * (T - n)  # attention launches of the timed streams
+    # attention launches of the timed steps
+    timed_launches = args.steps * Ly * sum(min(W, T - w0) - n for w0 in range(0, T, W))
     achieved = prof["attn_flop"] / (prof["attn_ms"] * 1e-3) / 1e12 if prof["attn_ms"] > 0 else 0.0
     clock = prof["attn_clock_ghz"]
     log(f"{fps:.1f} frames/s; attention {prof['attn_launches']} sampled launches, avg {attn_avg_ms * 1e3:.1f} us, "
@@ -213,6 +225,8 @@ def main():
     variant = [f"keyframe interval {args.keyframe_interval}"] if args.keyframe_interval != 1 else []
     variant += [f"S={S}"] if S != 6 else []
     variant += ["rotary Q/K"] if args.rotary else []
+    variant += [f"reset every {W} frames"] if W != T else []
+    variant += [f"{Ly} layers, M={M}, k={k}, T={T}"] if not variant else []
     result = {
         "metric": METRIC if default_workload(args) else f"GCA frames/s ({', '.join(variant)})",
         "value": round(fps, 2),
@@ -228,7 +242,8 @@ def main():
         "data": "synthetic (seeded N(0,1), resident pool of 64 frames per layer)",
         "config": {"workload": f"GCA direct-mode stream: {Ly} layers, H={H}, D={D}, M={M}+{S}, "
                                f"n={n}, k={k}, T={T}, keyframe interval {args.keyframe_interval}, bf16"
-                               + (", rotary Q/K" if args.rotary else ""),
+                               + (", rotary Q/K" if args.rotary else "")
+                               + (f", reset and anchor init every {W} frames" if W != T else ""),
                    "layers": Ly, "heads": H, "head_dim": D, "image_tokens": M,
                    "summary_tokens": S, "n_anchor": n, "k_window": k, "frames": T},
         "roofline": {
