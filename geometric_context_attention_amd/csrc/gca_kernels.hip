@@ -782,8 +782,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   const float c2 = a.scale_log2;
 
   // Ping-pong.  Every wave runs the same per-page sequence -- an MFMA phase
-  // (PV of page j-1, QK^T of page j), a barrier, a VALU phase (softmax of page
-  // j), a barrier -- but waves 4-7 (group B) start one barrier later than
+  // (QK^T of page j, then PV of page j-1 beside the exponent arguments of page
+  // j), a barrier, a VALU phase (the rest of page j's softmax), a barrier --
+  // but waves 4-7 (group B) start one barrier later than
   // waves 0-3 (group A).  The two groups share the SIMDs one to one, so while
   // one wave of a SIMD issues MFMAs the other works on the VALU.  Barriers
   // count arrivals, not code positions: in global phase 2j group A is in its
