@@ -854,11 +854,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   }
 }
 
-// Intra-frame attention of one (frame, head) per workgroup, the frame at
-// most kFrameTiles pages long: the frame's K tiles and V^T tiles are built
-// once in LDS from the input rows (rotated keys when rotary angles are
+// Intra-frame attention of one (frame, head, key split) per workgroup, the
+// frame at most kFrameTiles pages long: the split's K tiles and V^T tiles are
+// built once in LDS from the input rows (rotated keys when rotary angles are
 // given), so the page loop reads no memory.  The loop is the ping-pong of the
-// stream kernel without the copies; one split, final outputs.
+// stream kernel without the copies.  Batched launches run one split (final
+// outputs); a lone frame may split its pages (partials, then the merge).
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_in) {
   const AttnArgs a = batch_frame<2>(a_in);
@@ -871,6 +872,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   decode_wg(a, h, qb, s);
   const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int ppf = a.pl.ppf;  // <= kFrameTiles (checked at launch)
+  const int p0 = split_begin(a, s), np = split_begin(a, s + 1) - p0;  // this split's pages of the frame
   bf16x8 qf[NJ][4];
   load_q<NJ>(a, qf, h, qb, wave, l32, hf);
 
@@ -885,21 +887,23 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
     uint4 kv[kFrameTiles], vv[kFrameTiles];
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
-      const int valid = (j == ppf - 1) ? a.pl.f_last_valid : kPage;
+      const int pj = p0 + j;  // page of the frame
+      const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
       kv[j] = make_uint4(0u, 0u, 0u, 0u);
       vv[j] = kv[j];
-      if (j < ppf && row < valid) {
-        const size_t src = ((size_t)(j * kPage + row) * a.H + h) * kHeadDim + ch * 8;
+      if (j < np && row < valid) {
+        const size_t src = ((size_t)(pj * kPage + row) * a.H + h) * kHeadDim + ch * 8;
         kv[j] = *reinterpret_cast<const uint4*>(kin + src);
         vv[j] = *reinterpret_cast<const uint4*>(vin + src);
       }
     }
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
-      if (j < ppf) {
-        const int valid = (j == ppf - 1) ? a.pl.f_last_valid : kPage;
+      if (j < np) {
+        const int pj = p0 + j;
+        const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
         if (a.rope != nullptr && row < valid)
-          kv[j] = rope_bf16x8(kv[j], a.rope + (size_t)(j * kPage + row) * (kHeadDim / 2) + ch * 4);
+          kv[j] = rope_bf16x8(kv[j], a.rope + (size_t)(pj * kPage + row) * (kHeadDim / 2) + ch * 4);
         *reinterpret_cast<uint4*>(&lds[j][swz(row, ch)]) = kv[j];
         const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
 #pragma unroll
@@ -938,15 +942,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
       for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
   const bool grp_a = wave < 4;  // ping-pong as in k_attn_bf16
   if (!grp_a) wg_barrier();
-  for (int jj = 0; jj < ppf; ++jj) {
-    const int valid = (jj == ppf - 1) ? a.pl.f_last_valid : kPage;
+  for (int jj = 0; jj < np; ++jj) {
+    const int valid = (p0 + jj == ppf - 1) ? a.pl.f_last_valid : kPage;
     mfma_phase<NJ>(lds[jj], lds[jj == 0 ? 2 * kFrameTiles : kFrameTiles + jj - 1], qf, pf, o, sc, m, c2, valid,
                    l32, hf);
     wg_barrier();
     valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
     wg_barrier();
   }
-  mfma_phase<NJ>(nullptr, lds[kFrameTiles + ppf - 1], qf, pf, o, sc, m, c2, kPage, l32, hf);
+  mfma_phase<NJ>(nullptr, lds[kFrameTiles + np - 1], qf, pf, o, sc, m, c2, kPage, l32, hf);
   if (grp_a) wg_barrier();
 
   attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf);
@@ -1229,7 +1233,7 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   // intra-frame attention (every page fresh, one split, no cache bookkeeping)
   // of a frame that fits the LDS tiles: the LDS-resident frame kernel
   const bool frame = a.pl.a_cnt == 0 && a.pl.s_cnt == 0 && a.pl.w_cnt == 0 && a.fresh_frame < 0 &&
-                     a.nsplit == 1 && a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F;
+                     a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F;
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, g3, dim3(256), 0, st, a);
   else if (frame)

@@ -143,7 +143,7 @@ int gca_set_rotary(gca_ctx* ctx, const float* cos_sin);
  * each: a bf16 frame of at most 8 pages is held in LDS (up to 64 frames per
  * launch); longer frames and the fp32 mode go through scratch pages inside
  * the workspace (ceil(256 / (H * query blocks)) frames per launch, capped at
- * 64).  A lone frame splits its keys instead.
+ * 64).  A lone frame splits its keys instead (partials, then the merge).
  *   q, k, v: [frames, M+S, H, D] (device);  out: [frames, M+S, H, D] (device);
  *   lse: [frames, H, M+S] fp32 or NULL. */
 int gca_frame_attention(gca_ctx* ctx, const void* q, const void* k, const void* v, void* out,
