@@ -43,6 +43,18 @@ def check_outputs(o_gpu, o_ref, lse_gpu, lse_ref, mode, what=""):
     return max_abs, rel
 
 
+def rotate_as_cached(x, tab):
+    """Rotary rotation the way the cache stores it: x [..., H, D] (device),
+    tab [..., D/2, 2] fp32; each product and the sum rounded separately in
+    fp32 (no fused multiply-add), then rounded to x's dtype."""
+    x0, x1 = x[..., 0::2].float(), x[..., 1::2].float()
+    c, s = tab[..., None, :, 0], tab[..., None, :, 1]
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y.to(x.dtype)
+
+
 def swap23(s):
     s = np.asarray(s)
     return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)

@@ -13,11 +13,11 @@ import pytest
 import torch
 
 from geometric_context_attention_amd import _lib as G
-from geometric_context_attention_amd.synth import StreamSpec, draw_chunk
+from geometric_context_attention_amd.synth import StreamSpec, draw_chunk, rotary_table
 from oracle import gca_oracle as go
 from oracle.gca_oracle import GcaShape
 from oracle.page_model import PageModel
-from tests.gpu_util import check_outputs, check_state, say, to64
+from tests.gpu_util import check_outputs, check_state, rotate_as_cached, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -25,73 +25,98 @@ S, D, C = 6, 64, 32
 
 
 def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_offset_std=0.0,
-              heads=None, row_stride=1, bytes_at=()):
+              heads=None, row_stride=1, bytes_at=(), interval=1, rotary=False):
     F = M + S
     Tw = window_len or T
     spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=C,
                       key_offset_std=key_offset_std)
     cfg = G.make_config(num_heads=H, image_tokens=M, summary_tokens=S, n_anchor=n, k_window=k,
-                        max_frames=Tw, dtype=G.GCA_BF16)
+                        max_frames=Tw, dtype=G.GCA_BF16, keyframe_interval=interval)
     stack = G.GcaStack(cfg)
     pool = G.gca_plan(cfg, 0)["pool_pages"]
-    pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=pool, max_frames=Tw)
-    shp = GcaShape(M=M, n=n, k=k, S=S)
+    pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=pool, max_frames=Tw, m=interval)
+    shp = GcaShape(M=M, n=n, k=k, S=S, m=interval)
     scale = 1 / math.sqrt(D)
     hs = list(range(H)) if heads is None else list(heads)
-    keep_chunks = (min(k, Tw) + 1) // C + 2
+    keep_chunks = (min(k * interval, Tw) + 1) // C + 2  # the window spans k keyframes
     keep = {}
     sum_k = torch.empty((T, S, H, D), dtype=torch.bfloat16)
     sum_v = torch.empty((T, S, H, D), dtype=torch.bfloat16)
-    anc = None  # (q, k, v) of the current window's anchor frames, device
+    # Rotary angles use the frame index as time (synth recipe); summary rows
+    # sit at patch (0, 0), so their angles depend on the frame alone.
+    tab_sum = rotary_table(0, T, S, S) if rotary else None  # [T, S, D/2, 2]
+    tab_sum_d = tab_sum.cuda() if rotary else None
+    anc = None  # (q, k, v, angles) of the current window's anchor frames, device
     checked = 0
 
     def frame(g):
-        q, kk, v = keep[g // C]
+        q, kk, v, tab = keep[g // C]
         i = g % C
-        return q[i], kk[i], v[i]
+        return q[i], kk[i], v[i], (tab[i] if rotary else None)
+
+    def rot64(x, tab):
+        """fp64 rows [len, H, D], rotated by the given angles when rotary is on."""
+        x = to64(x)
+        return go.rotary(x, to64(tab)) if rotary else x
 
     def provider(w0, t):
         def get_rows(f, rows):
             rows = np.asarray(rows)
             g = w0 + f
-            if f < n or f >= t - k:
-                _, kk, v = frame(g) if f >= n else (None, anc[1][f], anc[2][f])
-                kr = kk[torch.as_tensor(rows, device=kk.device)][:, hs]
-                vr = v[torch.as_tensor(rows, device=v.device)][:, hs]
-                return to64(kr), to64(vr)
-            assert rows.max() < S, "trajectory frame asked for image rows"
-            return to64(sum_k[g, rows][:, hs]), to64(sum_v[g, rows][:, hs])
+            ri = torch.as_tensor(rows)
+            if rows.max() >= S:  # a full frame: anchor, window keyframe or the current frame
+                if f < n:
+                    kk, v, tab = anc[1][f], anc[2][f], (anc[3][f] if rotary else None)
+                else:
+                    assert g // C in keep, f"frame {g} left the kept chunks"
+                    _, kk, v, tab = frame(g)
+                rd = ri.to(kk.device)
+                kr = rot64(kk[rd], tab[rd] if rotary else None)
+                return kr[:, hs], to64(v[rd])[:, hs]
+            kr = rot64(sum_k[g, ri], tab_sum[g, ri] if rotary else None)
+            return kr[:, hs], to64(sum_v[g, ri])[:, hs]
         return get_rows
 
     def rows_batch(w0):
         def fn(fr, rw):
             out_k = torch.empty((len(fr), H, D), dtype=torch.bfloat16, device="cuda")
             out_v = torch.empty_like(out_k)
+            out_t = torch.empty((len(fr), D // 2, 2), dtype=torch.float32, device="cuda")
             summ = rw < S
             idx = np.nonzero(summ)[0]
             gi = torch.as_tensor(w0 + fr[idx])
             ri = torch.as_tensor(rw[idx])
-            out_k[torch.as_tensor(idx, device="cuda")] = sum_k[gi, ri].cuda()
-            out_v[torch.as_tensor(idx, device="cuda")] = sum_v[gi, ri].cuda()
+            di = torch.as_tensor(idx, device="cuda")
+            out_k[di] = sum_k[gi, ri].cuda()
+            out_v[di] = sum_v[gi, ri].cuda()
+            if rotary:
+                out_t[di] = tab_sum_d[gi.cuda(), ri.cuda()]
             for f in np.unique(fr[~summ]):
                 sel = np.nonzero((fr == f) & ~summ)[0]
                 if f < n:
-                    kk, v = anc[1][f], anc[2][f]
+                    kk, v, tab = anc[1][f], anc[2][f], (anc[3][f] if rotary else None)
                 else:
-                    _, kk, v = frame(w0 + f)
+                    _, kk, v, tab = frame(w0 + f)
                 r = torch.as_tensor(rw[sel], device="cuda")
-                out_k[torch.as_tensor(sel, device="cuda")] = kk[r]
-                out_v[torch.as_tensor(sel, device="cuda")] = v[r]
+                ds = torch.as_tensor(sel, device="cuda")
+                out_k[ds] = kk[r]
+                out_v[ds] = v[r]
+                if rotary:
+                    out_t[ds] = tab[r]
+            if rotary:
+                out_k = rotate_as_cached(out_k, out_t)
             return out_k, out_v
         return fn
 
     for g in range(T):
         if g % C == 0:
             c = g // C
-            keep[c] = draw_chunk(spec, layer, c, device="cuda")
+            q_c, k_c, v_c = draw_chunk(spec, layer, c, device="cuda")
+            tab_c = rotary_table(c * C, C, F, S).cuda() if rotary else None  # [C, F, D/2, 2]
+            keep[c] = (q_c, k_c, v_c, tab_c)
             hi = min(C, T - g)
-            sum_k[g:g + hi] = keep[c][1][:hi, :S].cpu()
-            sum_v[g:g + hi] = keep[c][2][:hi, :S].cpu()
+            sum_k[g:g + hi] = k_c[:hi, :S].cpu()
+            sum_v[g:g + hi] = v_c[:hi, :S].cpu()
             for old in [x for x in keep if x < c - keep_chunks]:
                 del keep[old]
         t = g % Tw
@@ -102,34 +127,43 @@ def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_o
         if t < n - 1:
             continue
         if t == n - 1:
-            qa = torch.stack([frame(w0 + f)[0] for f in range(n)]).reshape(n * F, H, D)
-            ka = torch.stack([frame(w0 + f)[1] for f in range(n)])
-            va = torch.stack([frame(w0 + f)[2] for f in range(n)])
-            anc = (qa, ka, va)
+            fa = [frame(w0 + f) for f in range(n)]
+            qa = torch.stack([x[0] for x in fa]).reshape(n * F, H, D)
+            ka = torch.stack([x[1] for x in fa])
+            va = torch.stack([x[2] for x in fa])
+            ta = torch.stack([x[3] for x in fa]) if rotary else None  # kept alive with anc
+            anc = (qa, ka, va, ta)
+            if rotary:
+                G.gca_set_rotary(stack.ctx, ta.reshape(n * F, D // 2, 2))
             out, lse = stack.anchor_init(0, qa, ka.reshape(n * F, H, D), va.reshape(n * F, H, D))
             pm.anchor_init()
             if g in samples:
-                ref, lref = go.anchor_init(to64(qa)[:, hs], to64(ka.reshape(n * F, H, D))[:, hs],
+                tq = ta.reshape(n * F, D // 2, 2) if rotary else None
+                ref, lref = go.anchor_init(rot64(qa, tq)[:, hs], rot64(ka.reshape(n * F, H, D), tq)[:, hs],
                                            to64(va.reshape(n * F, H, D))[:, hs], scale)
                 check_outputs(out[:, hs], ref, lse[hs], lref, "bf16", f"anchor init at frame {g}")
                 checked += 1
         else:
-            q, kk, v = frame(g)
+            q, kk, v, tab = frame(g)
+            if rotary:
+                G.gca_set_rotary(stack.ctx, tab)
             out, lse = stack.step(0, q, kk, v)
             pm.step(t)
             if g in samples:
                 rows = np.arange(0, F, row_stride)
-                ref, lref = go.step(t, to64(q)[rows][:, hs], provider(w0, t), shp, scale)
-                ma, rel = check_outputs(out[torch.as_tensor(rows, device="cuda")][:, hs], ref,
-                                        lse[hs][:, torch.as_tensor(rows, device="cuda")], lref,
+                rd = torch.as_tensor(rows, device="cuda")
+                qr = rot64(q[rd], tab[rd] if rotary else None)
+                ref, lref = go.step(t, qr[:, hs], provider(w0, t), shp, scale)
+                ma, rel = check_outputs(out[rd][:, hs], ref, lse[hs][:, rd], lref,
                                         "bf16", f"frame {g} (step {t})")
                 say(f"  frame {g}: keys {go.visible_key_count(t, shp)}, max-abs {ma:.2e}, rel {rel:.2e}")
                 checked += 1
         if g in state_at:
             check_state(stack, 0, pm, rows_of_batch=rows_batch(w0) if g in bytes_at else None)
+    if rotary:
+        G.gca_set_rotary(stack.ctx, None)
     assert checked == len(samples)
     stack.close()
-
 
 def test_paper_shape_one_layer_k16_correlated_keys():
     """M=500+6, 16 heads, n=3, k=16, T=10000, per-frame key offsets N(0, 0.5^2);
@@ -160,3 +194,18 @@ def test_full_causal_cache():
     T = 2000
     _fullsize(500, 3, T, T, 16, layer=0, samples={3, 1000, T - 1}, heads=(0, 7, 15), row_stride=4,
               state_at={1000, T - 1}, bytes_at={1000})
+
+
+@pytest.mark.parametrize("interval,rotary", [(4, True), (4, False), (1, True)])
+def test_keyframe_interval_and_rotary(interval, rotary):
+    """The benchmark's variants at the paper's shape: keyframe interval 4
+    (k=64 keyframes span 256 frames) and rotary angles on Q and cached K,
+    M=500+6, 16 heads, T=3000."""
+    T = 3000
+    # keyframe 3 keeps only its summary rows once 64 later keyframes are cached:
+    # from step 3 + 64 * interval + 1 on (68 for interval 1, 260 for interval 4)
+    first_old = 3 + 64 * interval + 1
+    _fullsize(500, 3, 64, T, 16, layer=3, interval=interval, rotary=rotary,
+              samples={2, 3, 4, 5, first_old - 1, first_old, first_old + 1, 1501, T - 1},
+              state_at={3, 4, first_old - 1, first_old, T - 1}, bytes_at={first_old, T - 1})
+

@@ -16,21 +16,11 @@ from geometric_context_attention_amd.synth import StreamSpec, draw_frames, rotar
 from oracle import gca_oracle as go
 from oracle.gca_oracle import GcaShape
 from oracle.page_model import PageModel
-from tests.gpu_util import check_outputs, check_state, say, to64
+from tests.gpu_util import check_outputs, check_state, rotate_as_cached, say, to64
 
 pytestmark = pytest.mark.gpu
 
 DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
-
-
-def _rotate(x, tab):
-    """x [..., F, H, D] (device), tab [..., F, D/2, 2] fp32: unfused fp32 rotation."""
-    x0, x1 = x[..., 0::2].float(), x[..., 1::2].float()
-    c, s = tab[..., None, :, 0], tab[..., None, :, 1]
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    y[..., 0::2] = x0 * c - x1 * s
-    y[..., 1::2] = x0 * s + x1 * c
-    return y.to(x.dtype)
 
 
 @pytest.mark.parametrize("mode,M,H,k,T", [("fp32", 32, 2, 4, 30), ("bf16", 181, 4, 3, 24)])
@@ -50,7 +40,7 @@ def test_stream_with_rotary(mode, M, H, k, T):
     o_ref, l_ref = go.stream_online(qr.reshape(T, F, H, 64), kr.reshape(T, F, H, 64), to64(v), shp,
                                     1 / math.sqrt(64))
     qd, kd, vd, td = q.cuda(), kx.cuda(), v.cuda(), tab.cuda()
-    k_cached = _rotate(kd, td)  # what the cache must hold
+    k_cached = rotate_as_cached(kd, td)  # what the cache must hold
     pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=G.gca_plan(cfg, 0)["pool_pages"], max_frames=T)
 
     def rows_of(f, rows):
