@@ -297,6 +297,10 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     sp = ctypes.c_void_p(stream.cuda_stream)
     fa = L.gca_frame_attention
     calls = [(t, min(B, T - t)) for t in range(0, T, B)]
+    # the kernel that runs the calls (see gca_frame_attention): up to 4 bf16
+    # frames of <= 8 pages one page per wave, more of them held in LDS
+    ppf = -(-F // 64)
+    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else "k_frame_attn_bf16") if ppf <= 8 else "k_attn_bf16"
 
     def run():
         for t, nb in calls:
@@ -342,7 +346,7 @@ def frame_attention_bench(args, cfg, G, torch, dev):
                                f"{B} frames per call, bf16", "frames_per_call": B},
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_attn_bf16",
+            "kernel": frame_kernel,
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

@@ -20,6 +20,9 @@ constexpr int kMaxFramePages = 32;  // pages of one frame passed by value (F <= 
 // kFrameBatchMax frames per launch.
 constexpr int kFrameTiles = 8;
 constexpr int kFrameBatchMax = 64;
+// Up to kWsplitBatchMax such frames per call run in a kernel that splits each
+// frame's pages over the waves of a workgroup (no key splits, no merge).
+constexpr int kWsplitBatchMax = 4;
 
 // Device-side state of one layer's cache, carved from the workspace.
 struct LayerDev {
@@ -125,6 +128,9 @@ hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int fr
                          const FramePages& pages, int ppf, int F, int H, bool f32,
                          const float2* rope, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st);
+// Intra-frame attention of bf16 frames of at most kFrameTiles pages, one page
+// per wave (a.nsplit must be 1; batch frames on grid rows).
+hipError_t launch_frame_wsplit(const AttnArgs& a, hipStream_t st);
 // Merge of the key splits (when a.nsplit > 1) and the eviction (when ev != null),
 // in one launch.
 hipError_t launch_merge_evict(const AttnArgs& a, const EvictPlan* ev, bool f32, hipStream_t st);

@@ -960,6 +960,210 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   }
 }
 
+// Intra-frame attention with the keys split over the waves of a workgroup:
+// one workgroup per (frame, head, 32-row query block), wave w takes page w
+// of the frame (keys 64w .. 64w+63).  The Q block and each wave's K page are
+// copied into swizzled LDS tiles with full-row (coalesced) copies; each wave
+// transposes its V page into an LDS tile of its own, then computes its
+// page's scores, their softmax against its own row max and the PV product.
+// The waves' (m, l, O) are combined in LDS in fp32.  Nothing passes through
+// memory between these steps and there is no merge launch, so a lone frame
+// costs one short launch: the latency-bound case (one frame per call) that
+// the page-pipelined frame kernel, built for many frames, does not serve well.
+constexpr int kWsRows = 32;           // query rows per workgroup
+constexpr int kWsPad = kHeadDim + 4;  // padded row of the O exchange: rows fall on different banks
+static_assert(kFrameTiles == kAttnWaves, "one page of the frame per wave");
+// LDS: Q tile (32 rows), then each wave's K tile and V^T tile; after the PV
+// products the O exchange reuses the space from the start
+constexpr int kWsQElems = kWsRows * kHeadDim;
+constexpr int kWsTilesBytes = (kWsQElems + 2 * kAttnWaves * kTileElems) * 2;
+constexpr int kWsExBytes = kAttnWaves * kWsRows * kWsPad * 4;
+static_assert(kWsExBytes <= kWsTilesBytes, "the O exchange fits in the tiles' space");
+
+// Copy rows r0 .. r0+7 of a 64-wide bf16 tile into LDS, swizzled (chunk c of
+// row r at swz(r, c)): lane l takes source chunk (l & 7) ^ ((r >> 1) & 7) of
+// row r0 + (l >> 3) into LDS position 8r + (l & 7); `src_row` gives the
+// row's address (rows past the valid ones repeat a valid one).
+template <class RowPtr>
+__device__ __forceinline__ void copy_rows8(uint16_t* tile, int r0, int lane, RowPtr src_row) {
+  const int r = r0 + (lane >> 3), pc = lane & 7;
+  __builtin_amdgcn_global_load_lds(src_row(r) + ((pc ^ ((r >> 1) & 7)) << 3), tile + r0 * kHeadDim, 16, 0, 0);
+}
+
+__global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs a_in) {
+  const AttnArgs a = batch_frame<2>(a_in);
+  constexpr int D = kHeadDim;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kWsTilesBytes];
+  __shared__ float2 mlx[kAttnWaves][kWsRows];  // each wave's (m, l) per query row
+  uint16_t* qt = reinterpret_cast<uint16_t*>(lds_raw);
+  auto kt_of = [&](int w) { return qt + kWsQElems + w * kTileElems; };
+  auto vt_of = [&](int w) { return qt + kWsQElems + (kAttnWaves + w) * kTileElems; };
+  auto ox = reinterpret_cast<float(*)[kWsRows][kWsPad]>(lds_raw);
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int qbs = (a.Lq + kWsRows - 1) / kWsRows;
+  const int h = blockIdx.x / qbs, qb = blockIdx.x - h * qbs;
+  const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
+  const int H = a.H, ppf = a.pl.ppf;  // ppf <= kAttnWaves (checked at launch)
+  // valid keys of this wave's page (0: the frame has fewer pages than waves)
+  const int valid = wave < ppf ? (wave == ppf - 1 ? a.pl.f_last_valid : kPage) : 0;
+  const int key0 = wave * kPage;
+  const uint16_t* qin = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
+  const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
+
+  // copies: waves 0-3 each take 8 rows of the Q block (rows past the frame
+  // repeat its last row; their outputs are not stored), every wave with keys
+  // its K page (rows past the valid ones repeat the last valid row: their
+  // scores are masked)
+  if (wave < kWsRows / 8)
+    copy_rows8(qt, wave * 8, lane, [&](int r) {
+      const int row = min(qb * kWsRows + r, a.Lq - 1);
+      return qin + ((size_t)row * H + h) * D;
+    });
+  uint4 vr[8];
+  const int cg = lane >> 3, ch = lane & 7;
+  if (valid > 0) {  // uniform
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      copy_rows8(kt_of(wave), i * 8, lane, [&](int r) {
+        return kin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
+      });
+    // V rows for the transposition: lane (cg, ch) fills V^T chunk cg
+    // (columns 8cg .. 8cg+7) of rows d = 8ch .. 8ch+7.  Column 8cg + i holds
+    // key swap23(8cg + i) = 16(cg >> 1) + 8(i >> 2) + 4(cg & 1) + i % 4, whose
+    // 16-byte chunk ch of V it loads; keys past the valid ones are zero.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = 16 * (cg >> 1) + 8 * (i >> 2) + 4 * (cg & 1) + (i & 3);
+      vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (key < valid) vr[i] = *reinterpret_cast<const uint4*>(vin + ((size_t)(key0 + key) * H + h) * D + ch * 8);
+    }
+    // V^T element (d, col), col = swap23(key), at swz(d, col / 8) + col % 8 as
+    // in the pool: one 16-byte store per row d, word w = loads 2w and 2w+1
+    uint16_t* vt = vt_of(wave);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x0 = (&vr[2 * w].x)[e >> 1], x1 = (&vr[2 * w + 1].x)[e >> 1];
+        wd[w] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+      }
+      *reinterpret_cast<uint4*>(&vt[swz(ch * 8 + e, cg)]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+  }
+  GCA_WAIT_VMCNT(0);  // this wave's copies have landed
+  __syncthreads();    // and every wave's: the Q tile comes from waves 0-3
+
+  // Q^T fragments: query row qb*32 + l32, d = 16c + 8hf .. +7
+  const int qrow = qb * kWsRows + l32;
+  bf16x8 qf[1][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint4 v = *reinterpret_cast<const uint4*>(&qt[swz(l32, c * 2 + hf)]);
+    if (a.rope != nullptr && qrow < a.Lq) v = rope_bf16x8(v, a.rope + (size_t)qrow * (D / 2) + c * 8 + hf * 4);
+    qf[0][c] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  float mrow = -INFINITY, lrow = 0.f;  // this wave's row max (log2 units) and row sum for query l32
+  f32x16 o[2][1];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][0][r] = 0.f;
+  if (valid > 0) {  // uniform
+    const uint16_t* kt_ = kt_of(wave);
+    f32x16 sc[2][1];
+    const f32x16 zero = {};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // K fragment: key 32kt + l32 of the page, d = 16c + 8hf .. +7
+        const int key = kt * 32 + l32;
+        uint4 kv = *reinterpret_cast<const uint4*>(&kt_[swz(key, c * 2 + hf)]);
+        if (a.rope != nullptr && key < valid)
+          kv = rope_bf16x8(kv, a.rope + (size_t)(key0 + key) * (D / 2) + c * 8 + hf * 4);
+        sc[kt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[0][c],
+                                                            c == 0 ? zero : sc[kt][0], 0, 0, 0);
+      }
+    if (valid < kPage) mask_page<1>(sc, valid, hf);
+    // row max of the page (key 0 is always valid), then P = exp2(s c2 - m)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt][0][r]);
+    mrow = half_pair_max(mx) * a.scale_log2;
+    bf16x8 pf[1][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        pf[0][kt * 2 + (r >> 3)][r & 7] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][0][r], a.scale_log2, -mrow));
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float acc = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pf[0][kc][e], pf[0][kc][e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+      }
+    lrow = half_pair_sum(acc);
+    // O^T += V^T P^T: fragment i is d-tile i % 2, 16-key chunk i / 2
+    const uint16_t* vt = vt_of(wave);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+      o[i % 2][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][i / 2], o[i % 2][0], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with the tiles: the exchange reuses them
+  // exchange: register r of d-tile dt holds d = 32dt + 8(r/4) + 4hf + r%4 of query l32
+  if (hf == 0) mlx[wave][l32] = make_float2(mrow, lrow);
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(&ox[wave][l32][dt * 32 + 8 * g + 4 * hf]) =
+          make_float4(o[dt][0][4 * g], o[dt][0][4 * g + 1], o[dt][0][4 * g + 2], o[dt][0][4 * g + 3]);
+  __syncthreads();
+  // combine: thread t finishes query q = t / 16, d = 4 (t % 16) .. +3
+  const int q = tid >> 4, d4 = (tid & 15) * 4;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, mlx[w][q].x);
+  float L = 0.f, r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kAttnWaves; ++w) {
+    const float2 e = mlx[w][q];
+    const float sw = __builtin_amdgcn_exp2f(e.x - M);  // 0 for a wave without keys (m = -inf)
+    const float4 v = *reinterpret_cast<const float4*>(&ox[w][q][d4]);
+    L += sw * e.y;
+    r0 += sw * v.x;
+    r1 += sw * v.y;
+    r2 += sw * v.z;
+    r3 += sw * v.w;
+  }
+  const int row = qb * kWsRows + q;
+  if (row < a.Lq) {
+    const float inv = 1.f / L;
+    uint2 w;
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(r0 * inv)) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(r1 * inv)) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(r2 * inv)) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(r3 * inv)) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * H + h) * D + d4) = w;
+    if (a.lse != nullptr && (tid & 15) == 0) a.lse[(size_t)h * a.Lq + row] = M * kLn2 + logf(L);
+  }
+  if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
+    atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
+  }
+}
+
 // fp32 attention: one thread per query row (256-row blocks).  Each page is
 // staged in LDS; keys are taken one at a time with an online softmax.
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a_in) {
@@ -1240,6 +1444,14 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
     hipLaunchKernelGGL(k_frame_attn_bf16, g3, dim3(kAttnWaves * 64), 0, st, a);
   else
     hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, g3, dim3(kAttnWaves * 64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_wsplit(const AttnArgs& a, hipStream_t st) {
+  if (a.batch < 1 || a.nsplit != 1 || a.pl.ppf < 1 || a.pl.ppf > kAttnWaves || a.Lq != a.F || a.H < 1)
+    return hipErrorInvalidValue;
+  const dim3 g3(a.H * ((a.Lq + kWsRows - 1) / kWsRows), a.batch);
+  hipLaunchKernelGGL(k_frame_wsplit_bf16, g3, dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -283,8 +283,11 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.F = c->g.F;
   a.qblocks = (int)cdiv(Lq, query_rows(cfg));
   const int64_t npg = (int64_t)pl.a_cnt + pl.s_cnt + pl.w_cnt + pl.fresh_cnt;
+  // intra-frame attention of a few bf16 frames that fit the LDS tiles: one
+  // page per wave, no key splits
+  const bool wsplit = use_scratch && !c->f32 && c->g.ppf <= kFrameTiles && batch <= kWsplitBatchMax;
   // a batched launch (intra-frame attention) runs one split per frame
-  a.nsplit = batch > 1 ? 1 : choose_splits(cfg, a.qblocks, npg);
+  a.nsplit = batch > 1 || wsplit ? 1 : choose_splits(cfg, a.qblocks, npg);
   a.batch = batch;
   a.scale = c->g.scale;
   a.scale_log2 = (float)(c->g.scale * 1.4426950408889634);
@@ -307,7 +310,7 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
     hipError_t r = hipEventRecord(ep->a, st);
     if (r != hipSuccess) return hip_fail(r, "hipEventRecord");
   }
-  hipError_t e = launch_attention(a, c->f32, st);
+  hipError_t e = wsplit ? launch_frame_wsplit(a, st) : launch_attention(a, c->f32, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   if (ep != nullptr) {
     hipError_t r = hipEventRecord(ep->b, st);

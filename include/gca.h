@@ -139,11 +139,14 @@ int gca_set_rotary(gca_ctx* ctx, const float* cos_sin);
  * GCA layers: technical summary §2.1; news article, pipeline figure): full,
  * unmasked softmax attention of each frame's M+S tokens among themselves,
  * for `frames` frames.  Uses the context's shape, dtype and scale; no
- * layer's cache is read or changed.  Several frames go in batches, one launch
- * each: a bf16 frame of at most 8 pages is held in LDS (up to 64 frames per
- * launch); longer frames and the fp32 mode go through scratch pages inside
- * the workspace (ceil(256 / (H * query blocks)) frames per launch, capped at
- * 64).  A lone frame splits its keys instead (partials, then the merge).
+ * layer's cache is read or changed.  Frames go in batches, one launch each.
+ * bf16 frames of at most 8 pages: a call of up to 4 frames runs one page per
+ * wave of a workgroup (32 query rows per workgroup, the waves' partial
+ * softmax results combined in LDS: no scratch, no merge launch); larger calls
+ * hold each frame in LDS, up to 64 frames per launch.  Longer frames and the
+ * fp32 mode go through scratch pages inside the workspace
+ * (ceil(256 / (H * query blocks)) frames per launch, capped at 64; a lone
+ * such frame splits its keys, then the merge).
  *   q, k, v: [frames, M+S, H, D] (device);  out: [frames, M+S, H, D] (device);
  *   lse: [frames, H, M+S] fp32 or NULL. */
 int gca_frame_attention(gca_ctx* ctx, const void* q, const void* k, const void* v, void* out,

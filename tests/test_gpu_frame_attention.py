@@ -2,9 +2,11 @@
 
 Frames of the stream shapes (M = 500 and a ragged M), bf16 and fp32, are
 attended within themselves through the C ABI and compared with the fp64
-oracle: a lone frame (the split-K path); bf16 frames of up to 8 pages (the
-kernel that holds a frame in LDS, 64 frames per launch, so 70 frames make a
-partial second batch); longer bf16 frames (M = 700: 12 pages, through
+oracle: bf16 calls of up to 4 frames of up to 8 pages (one page per wave
+of a workgroup, combined in LDS: a lone frame, ragged and full last pages,
+frames with fewer pages than waves, a 7-row frame); longer bf16 calls of up
+to 8 pages per frame (the kernel that holds a frame in LDS, 64 frames per
+launch, so 70 frames make a partial second batch); longer bf16 frames (M = 700: 12 pages, through
 scratch pages, 8 frames per launch at H = 16); fp32 (64 frames per launch
 at H = 4); and the benchmark's launch, 64 frames of M = 500 at H = 16; the call must leave every layer's cache untouched, so a stream
 interleaving frame attention with GCA steps still matches the oracle and its
@@ -29,7 +31,9 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 @pytest.mark.parametrize("mode,M,H,B", [("bf16", 500, 16, 3), ("bf16", 181, 4, 5), ("fp32", 58, 2, 4),
                                          ("bf16", 500, 16, 1), ("bf16", 500, 16, 21), ("fp32", 120, 4, 70),
-                                         ("bf16", 120, 4, 70), ("bf16", 700, 16, 10), ("bf16", 500, 16, 64)])
+                                         ("bf16", 120, 4, 70), ("bf16", 700, 16, 10), ("bf16", 500, 16, 64),
+                                         ("bf16", 181, 4, 2), ("bf16", 58, 2, 4), ("bf16", 506, 16, 1),
+                                         ("bf16", 1, 2, 3), ("bf16", 250, 8, 4), ("bf16", 500, 16, 5)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6
