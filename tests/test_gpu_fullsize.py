@@ -21,11 +21,11 @@ from tests.gpu_util import check_outputs, check_state, rotate_as_cached, say, to
 
 pytestmark = pytest.mark.gpu
 
-S, D, C = 6, 64, 32
+D, C = 64, 32
 
 
 def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_offset_std=0.0,
-              heads=None, row_stride=1, bytes_at=(), interval=1, rotary=False):
+              heads=None, row_stride=1, bytes_at=(), interval=1, rotary=False, S=6):
     F = M + S
     Tw = window_len or T
     spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=C,
@@ -209,3 +209,10 @@ def test_keyframe_interval_and_rotary(interval, rotary):
               samples={2, 3, 4, 5, first_old - 1, first_old, first_old + 1, 1501, T - 1},
               state_at={3, 4, first_old - 1, first_old, T - 1}, bytes_at={first_old, T - 1})
 
+
+def test_one_summary_token():
+    """S = 1 (camera token only): M=500+1, 16 heads, k=64, T=3000; 64 old
+    frames share a summary page."""
+    T = 3000
+    _fullsize(500, 3, 64, T, 16, layer=5, S=1, samples={2, 3, 67, 68, 69, 131, 132, 1501, T - 1},
+              state_at={68, 131, 132, T - 1}, bytes_at={132, T - 1})
