@@ -882,20 +882,29 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   {
     const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
     const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
-    const int row = tid >> 3, ch = tid & 7;  // one 16-byte chunk of a 64x64 tile per thread
-    const int col = swap23(row);
-    uint4 kv[kFrameTiles], vv[kFrameTiles];
+    const int row = tid >> 3, ch = tid & 7;  // K: one 16-byte chunk of each tile per thread
+    // V: wave w transposes page w of the split; lane (cg, ch) = (lane >> 3,
+    // lane & 7) fills V^T chunk cg (columns 8cg .. 8cg+7) of rows d = 8ch ..
+    // 8ch+7.  Column 8cg + i holds slot swap23(8cg + i) = 16(cg >> 1) +
+    // 8(i >> 2) + 4(cg & 1) + i % 4, whose 16-byte chunk ch it loads.
+    const int cg = lane >> 3;
+    const int vpj = p0 + wave;
+    const int vvalid = wave < np ? ((vpj == ppf - 1) ? a.pl.f_last_valid : kPage) : 0;
+    uint4 kv[kFrameTiles], vr[8];
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
       const int pj = p0 + j;  // page of the frame
       const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
       kv[j] = make_uint4(0u, 0u, 0u, 0u);
-      vv[j] = kv[j];
-      if (j < np && row < valid) {
-        const size_t src = ((size_t)(pj * kPage + row) * a.H + h) * kHeadDim + ch * 8;
-        kv[j] = *reinterpret_cast<const uint4*>(kin + src);
-        vv[j] = *reinterpret_cast<const uint4*>(vin + src);
-      }
+      if (j < np && row < valid)
+        kv[j] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pj * kPage + row) * a.H + h) * kHeadDim + ch * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int slot = 16 * (cg >> 1) + 8 * (i >> 2) + 4 * (cg & 1) + (i & 3);
+      vr[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (slot < vvalid)
+        vr[i] = *reinterpret_cast<const uint4*>(vin + ((size_t)(vpj * kPage + slot) * a.H + h) * kHeadDim + ch * 8);
     }
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
@@ -905,12 +914,18 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
         if (a.rope != nullptr && row < valid)
           kv[j] = rope_bf16x8(kv[j], a.rope + (size_t)(pj * kPage + row) * (kHeadDim / 2) + ch * 4);
         *reinterpret_cast<uint4*>(&lds[j][swz(row, ch)]) = kv[j];
-        const uint32_t w[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+      }
+    }
+    if (wave < np) {  // uniform
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = ch * 8 + e;
-          lds[kFrameTiles + j][swz(d, col >> 3) + (col & 7)] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+      for (int e = 0; e < 8; ++e) {
+        uint32_t wd[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = (&vr[2 * w].x)[e >> 1], x1 = (&vr[2 * w + 1].x)[e >> 1];
+          wd[w] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
         }
+        *reinterpret_cast<uint4*>(&lds[kFrameTiles + wave][swz(ch * 8 + e, cg)]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
       }
     }
     static_assert(kTileElems * 2 == kAttnWaves * 64 * 16, "one 16-byte store per thread clears a tile");
