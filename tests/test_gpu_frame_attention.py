@@ -7,7 +7,7 @@ of a workgroup, combined in LDS: a lone frame, ragged and full last pages,
 frames with fewer pages than waves, a 7-row frame); longer bf16 calls of up
 to 8 pages per frame (the kernel that holds a frame in LDS, 64 frames per
 launch, so 70 frames make a partial second batch); longer bf16 frames (M = 700: 12 pages, through
-scratch pages, 8 frames per launch at H = 16); fp32 (64 frames per launch
+scratch pages, 8 frames per launch at H = 16; the largest frame, 2048 rows); fp32 (64 frames per launch
 at H = 4); and the benchmark's launch, 64 frames of M = 500 at H = 16; the call must leave every layer's cache untouched, so a stream
 interleaving frame attention with GCA steps still matches the oracle and its
 page state stays bit-exact.
@@ -33,7 +33,8 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
                                          ("bf16", 500, 16, 1), ("bf16", 500, 16, 21), ("fp32", 120, 4, 70),
                                          ("bf16", 120, 4, 70), ("bf16", 700, 16, 10), ("bf16", 500, 16, 64),
                                          ("bf16", 181, 4, 2), ("bf16", 58, 2, 4), ("bf16", 506, 16, 1),
-                                         ("bf16", 1, 2, 3), ("bf16", 250, 8, 4), ("bf16", 500, 16, 5)])
+                                         ("bf16", 1, 2, 3), ("bf16", 250, 8, 4), ("bf16", 500, 16, 5),
+                                         ("bf16", 2042, 2, 3), ("fp32", 2042, 1, 2)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6

@@ -98,6 +98,17 @@ def test_bf16_window_covers_stream():
     _run_stream("bf16", M=70, n=2, k=50, T=25, H=2, state_every=6)
 
 
+@pytest.mark.parametrize("M,n,k,T,H", [
+    (2042, 1, 2, 6, 2),    # the largest frame: 2048 rows, 32 pages, four 512-row query blocks
+    (122, 2, 3, 16, 2),    # frames end on a page boundary (two full pages)
+    (1, 3, 2, 12, 2),      # 7-row frames
+    (100, 2, 3, 12, 32),   # 32 heads: fewer key splits per head
+])
+def test_bf16_edge_shapes(M, n, k, T, H):
+    """Frame sizes and head counts at the edges of what the library accepts."""
+    _run_stream("bf16", M=M, n=n, k=k, T=T, H=H, state_every=1)
+
+
 def test_bf16_sharpened_queries():
     """Q scaled by 4 makes the softmax peaked (|O| ~ 1), so the max-abs gate bites."""
     _run_stream("bf16", M=120, n=3, k=4, T=24, H=2, q_scale=4.0, state_every=8, check_bytes=False)
