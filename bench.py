@@ -375,11 +375,21 @@ def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
     from geometric_context_attention_amd.synth import StreamSpec, draw_frames
     from oracle import gca_oracle as go
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+                                 for i in pools if i.get("user_api") == "blas"})) or blas
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:  # pragma: no cover
+        pass
     shp = go.GcaShape(M=M, n=n, k=k, S=S)
     F = M + S
     R = 16
@@ -418,6 +428,8 @@ def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
         "unit": "frames/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu": cpu,
+        "blas": blas,
         "sample": (f"fp64 numpy oracle, one layer: anchor init + steps t={[s[2] for s in samples]} "
                    f"({spent:.1f} s); time linear in keys fitted and summed over t={n}..{T - 1}, "
                    f"x{Ly} layers (extrapolated)"),
