@@ -854,12 +854,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   }
 }
 
-// Intra-frame attention of one (frame, head, key split) per workgroup, the
-// frame at most kFrameTiles pages long: the split's K tiles and V^T tiles are
-// built once in LDS from the input rows (rotated keys when rotary angles are
-// given), so the page loop reads no memory.  The loop is the ping-pong of the
-// stream kernel without the copies.  Batched launches run one split (final
-// outputs); a lone frame may split its pages (partials, then the merge).
+// Intra-frame attention of one (frame, head) per workgroup, the frame at most
+// kFrameTiles pages long: its K tiles and V^T tiles are built once in LDS from
+// the input rows (rotated keys when rotary angles are given), so the page loop
+// reads no memory.  The loop is the ping-pong of the stream kernel without the
+// copies.  Launches batch frames on grid rows and run one split (final
+// outputs).
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_in) {
   const AttnArgs a = batch_frame<2>(a_in);
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   decode_wg(a, h, qb, s);
   const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int ppf = a.pl.ppf;  // <= kFrameTiles (checked at launch)
-  const int p0 = split_begin(a, s), np = split_begin(a, s + 1) - p0;  // this split's pages of the frame
+  const int p0 = 0, np = ppf;  // one split: every page of the frame
   bf16x8 qf[NJ][4];
   load_q<NJ>(a, qf, h, qb, wave, l32, hf);
 
@@ -1452,7 +1452,7 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   // intra-frame attention (every page fresh, one split, no cache bookkeeping)
   // of a frame that fits the LDS tiles: the LDS-resident frame kernel
   const bool frame = a.pl.a_cnt == 0 && a.pl.s_cnt == 0 && a.pl.w_cnt == 0 && a.fresh_frame < 0 &&
-                     a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F;
+                     a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F && a.nsplit == 1;
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, g3, dim3(256), 0, st, a);
   else if (frame)
