@@ -646,53 +646,61 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, bf16x8 (&qf)[NJ][4], i
 
 // Outputs of a bf16 attention workgroup: with one split, O / l rounded to
 // bf16 and the LSE (natural log); otherwise the split's partial, O / l
-// rounded to bf16 with (m, l) in fp32 (m in log2 units).
+// rounded to bf16 with (m, l) in fp32 (m in log2 units).  Each wave first
+// writes its 64 rows into its own 8 KB LDS tile `stage` (16-byte chunk c of
+// row r at chunk c ^ (r & 7)), then stores them as whole 128-byte rows, eight
+// lanes per row: the register layout spreads a row over 32 lanes in 8-byte
+// pieces, and storing that directly touches 32 rows per store instruction.
+// The caller makes sure no other wave still reads or fills `stage`.
 template <int NJ>
 __device__ __forceinline__ void attn_epilogue(const AttnArgs& a, const f32x16 (&o)[2][NJ], const float (&m)[NJ],
-                                              float (&l)[NJ], int h, int qb, int s, int wave, int l32, int hf) {
+                                              float (&l)[NJ], int h, int qb, int s, int wave, int l32, int hf,
+                                              uint16_t* stage) {
   constexpr int D = kHeadDim;
   const int H = a.H;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) l[j] = half_pair_sum(l[j]);
   const bool final_out = a.nsplit == 1;
+  const int row0 = qb * kQBlock + wave * 64;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int row = qb * kQBlock + wave * 64 + j * 32 + l32;
-    if (final_out) {
-      if (row < a.Lq) {
-        const float inv = 1.f / l[j];
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * H + h) * D;
+    const int rr = j * 32 + l32;  // row of the wave's tile
+    const float inv = 1.f / l[j];
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = dt * 32 + 8 * g + 4 * hf;
-            __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
-            __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
-            uint2 w;
-            w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
-            w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
-            *reinterpret_cast<uint2*>(out + d) = w;
-          }
-        if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * kLn2 + logf(l[j]);
+      for (int g = 0; g < 4; ++g) {
+        // d = 32dt + 8g + 4hf .. +3: half hf of chunk 4dt + g
+        const __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
+        const __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
+        uint2 w;
+        w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
+        w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
+        *reinterpret_cast<uint2*>(&stage[rr * 64 + (((4 * dt + g) ^ (rr & 7)) << 3) + 4 * hf]) = w;
       }
-    } else if (row < a.Lq) {
-      // split partial: O / l rounded to bf16, with (m, l) in fp32
-      const float inv = 1.f / l[j];
-      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+    const int row = row0 + rr;
+    if (row < a.Lq && hf == 0) {
+      if (final_out) {
+        if (a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = m[j] * kLn2 + logf(l[j]);
+      } else {
+        a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
+      }
+    }
+  }
+  // the tile is this wave's alone: its own stores must land before its reads
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  const int c = l32 & 7;  // lane: 16-byte chunk c of row 8i + (lane >> 3)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = dt * 32 + 8 * g + 4 * hf;
-          __bf16 b0v = (__bf16)(o[dt][j][4 * g + 0] * inv), b1v = (__bf16)(o[dt][j][4 * g + 1] * inv);
-          __bf16 b2v = (__bf16)(o[dt][j][4 * g + 2] * inv), b3v = (__bf16)(o[dt][j][4 * g + 3] * inv);
-          uint2 w;
-          w.x = (uint32_t)__builtin_bit_cast(uint16_t, b0v) | ((uint32_t)__builtin_bit_cast(uint16_t, b1v) << 16);
-          w.y = (uint32_t)__builtin_bit_cast(uint16_t, b2v) | ((uint32_t)__builtin_bit_cast(uint16_t, b3v) << 16);
-          *reinterpret_cast<uint2*>(po + d) = w;
-        }
-      if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], l[j]);
+  for (int i = 0; i < 64 / 8; ++i) {
+    const int rr = i * 8 + ((hf * 32 + l32) >> 3);
+    const int row = row0 + rr;
+    const uint4 v = *reinterpret_cast<const uint4*>(&stage[rr * 64 + ((c ^ (rr & 7)) << 3)]);
+    if (row < a.Lq) {
+      uint16_t* dst = final_out
+                          ? reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * H + h) * D
+                          : reinterpret_cast<uint16_t*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+      *reinterpret_cast<uint4*>(dst + c * 8) = v;
     }
   }
 }
@@ -846,8 +854,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], qf, pf, o, sc, m, c2, kPage, l32, hf);
   if (GCA_PINGPONG && grp_a) wg_barrier();
   GCA_WAIT_VMCNT(0);  // no copy into LDS outlives the workgroup
+  __syncthreads();    // every wave's copies have landed and its last PV has read the ring
 
-  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf);
+  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf, &ring[wave][0]);
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
@@ -967,8 +976,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   }
   mfma_phase<NJ>(nullptr, lds[kFrameTiles + np - 1], qf, pf, o, sc, m, c2, kPage, l32, hf);
   if (grp_a) wg_barrier();
+  __syncthreads();  // every wave's last PV has read the tiles
 
-  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf);
+  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf, &lds[wave][0]);
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
