@@ -68,10 +68,11 @@ def test_stream_with_rotary(mode, M, H, k, T):
     stack.close()
 
 
-@pytest.mark.parametrize("mode", ["bf16", "fp32"])
-def test_frame_attention_with_rotary(mode):
+@pytest.mark.parametrize("mode,B", [("bf16", 3), ("bf16", 6), ("fp32", 3)])
+def test_frame_attention_with_rotary(mode, B):
+    """3 bf16 frames: one page per wave; 6: each frame held in LDS; fp32: scratch pages."""
     gdt, tdt = DT[mode]
-    M, S, H, B = 250, 6, 4, 3
+    M, S, H = 250, 6, 4
     F = M + S
     cfg = G.make_config(num_heads=H, image_tokens=M, summary_tokens=S, n_anchor=3, k_window=2,
                         max_frames=8, dtype=gdt)
