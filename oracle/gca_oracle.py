@@ -56,7 +56,6 @@ on any page, so beyond those pins the oracle itself is the reference.
 """
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -156,10 +155,6 @@ def offline_mask(T: int, shp: GcaShape) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------
-
-def default_scale(D: int) -> float:
-    return 1.0 / math.sqrt(D)
-
 
 def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                      mask: np.ndarray | None, scale: float):

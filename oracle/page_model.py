@@ -37,7 +37,6 @@ and the computed peak pool size).
 """
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass, field
 
 
@@ -227,7 +226,3 @@ class PageModel:
         else:
             assert t == max(self.frame_pages)
         return out
-
-
-def summary_pages_for(n_traj: int, S: int, P: int) -> int:
-    return math.ceil(S * n_traj / P)
