@@ -18,11 +18,19 @@ The JSON line also carries:
   workload (one layer, a few sampled steps, linear in the key count) and
   extrapolated to the whole stream.
 
-Non-default workloads (each prints its own line, without cpu_baseline):
---keyframe-interval m (frames between keyframes), --summary-tokens S,
---rotary (rotary angles applied to Q and to K as it is cached), and
---workload frame-attention (the intra-frame layers through
-gca_frame_attention, --frames-per-call frames per call).
+The other stream configurations the step is quoted on, each one line with
+its own cpu_baseline (--config N sets the flags):
+  1  tiny fp32 stream: 1 layer, 2 heads, M=32+6, n=3, k=4, T=64
+  2  one layer at the paper's token shape, k=16, per-frame key offsets
+     N(0, 0.5^2), T=10000 (69.5k cached tokens at the end)
+  3  the default line above
+  4  full causal cache: k >= T, T=2000, 12 layers (1.01M keys at the end)
+  5  dense grid: M=999+6, reset and anchor init every 128 frames, 12 layers
+
+Variants of the stream (no cpu_baseline): --keyframe-interval m (frames
+between keyframes), --summary-tokens S, --rotary (rotary angles applied to Q
+and to K as it is cached), and --workload frame-attention (the intra-frame
+layers through gca_frame_attention, --frames-per-call frames per call).
 """
 from __future__ import annotations
 
@@ -39,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_CLOCK_GHZ = 2.4   # the clock the published peak is quoted at
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 (matrix cores and vector units alike)
 PEAK_HBM_GBS = 8000.0
 PROFILE_EVERY = 13     # attention launches per timed sample
 METRIC = "GCA frames/s (12 layers, M=500,n=3,k=64,T=10k) + % of bf16 MFMA peak"
@@ -49,10 +58,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1, help="timed streams")
     ap.add_argument("--warmup", type=int, default=1, help="untimed streams before timing")
+    ap.add_argument("--config", type=int, choices=[1, 2, 3, 4, 5], default=0,
+                    help="preset of one of the five stream configurations (sets the flags below)")
     ap.add_argument("--frames", type=int, default=10000, help="T (frames per stream)")
     ap.add_argument("--layers", type=int, default=12)
     ap.add_argument("--window", type=int, default=64)
     ap.add_argument("--image-tokens", type=int, default=500)
+    ap.add_argument("--heads", type=int, default=16)
+    ap.add_argument("--dtype", choices=["bf16", "fp32"], default="bf16")
+    ap.add_argument("--key-offset-std", type=float, default=0.0,
+                    help="std of the per-frame offset added to every key row of a frame")
     ap.add_argument("--pool", type=int, default=64, help="resident input frames per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU sample")
@@ -67,13 +82,36 @@ def parse():
                     help="windows of R frames: reset and anchor init at the start of each")
     ap.add_argument("--frames-per-call", type=int, default=16,
                     help="frames per gca_frame_attention call (frame-attention workload)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    presets = {
+        1: dict(layers=1, heads=2, image_tokens=32, window=4, frames=64, dtype="fp32", pool=64),
+        2: dict(layers=1, window=16, key_offset_std=0.5),
+        3: {},
+        4: dict(window=2000, frames=2000),
+        5: dict(image_tokens=999, reset_every=128),
+    }
+    for key, val in presets.get(args.config, {}).items():
+        setattr(args, key, val)
+    return args
 
 
 def default_workload(args):
     return (args.workload == "stream" and args.keyframe_interval == 1 and args.summary_tokens == 6
             and not args.rotary and args.reset_every == 0 and args.layers == 12 and args.window == 64
-            and args.frames == 10000 and args.image_tokens == 500)
+            and args.frames == 10000 and args.image_tokens == 500 and args.heads == 16
+            and args.dtype == "bf16" and args.key_offset_std == 0.0)
+
+
+def config_workload(args):
+    """The numbered stream configuration these flags are, or 0."""
+    if (args.workload != "stream" or args.keyframe_interval != 1 or args.summary_tokens != 6
+            or args.rotary):
+        return 0
+    shape = (args.layers, args.heads, args.image_tokens, args.window, args.frames, args.dtype,
+             args.key_offset_std, args.reset_every)
+    return {(1, 2, 32, 4, 64, "fp32", 0.0, 0): 1, (1, 16, 500, 16, 10000, "bf16", 0.5, 0): 2,
+            (12, 16, 500, 64, 10000, "bf16", 0.0, 0): 3, (12, 16, 500, 2000, 2000, "bf16", 0.0, 0): 4,
+            (12, 16, 999, 64, 10000, "bf16", 0.0, 128): 5}.get(shape, 0)
 
 
 def copy_calibration(mib):
@@ -116,15 +154,18 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    H, D, M, S, n = 16, 64, args.image_tokens, args.summary_tokens, 3
+    H, D, M, S, n = args.heads, 64, args.image_tokens, args.summary_tokens, 3
     k, T, Ly = args.window, args.frames, args.layers
     F = M + S
+    f32 = args.dtype == "fp32"
+    tdt = torch.float32 if f32 else torch.bfloat16
+    esz = 4 if f32 else 2
     W = args.reset_every if args.reset_every > 0 else T  # frames per window (state reset between)
     if W <= n or 0 < T % W <= n:
         print("--reset-every: every window must hold more than the 3 anchor frames", file=sys.stderr)
         sys.exit(2)
     cfg = G.make_config(num_layers=Ly, num_heads=H, head_dim=D, image_tokens=M, summary_tokens=S,
-                        n_anchor=n, k_window=k, max_frames=W, dtype=G.GCA_BF16,
+                        n_anchor=n, k_window=k, max_frames=W, dtype=G.GCA_FP32 if f32 else G.GCA_BF16,
                         keyframe_interval=args.keyframe_interval)
     if args.workload == "frame-attention":
         return frame_attention_bench(args, cfg, G, torch, dev)
@@ -138,16 +179,17 @@ def main():
     R = args.pool
     pools = []
     for layer in range(Ly):
-        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=32)
+        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=tdt, seed=0, chunk=32,
+                          key_offset_std=args.key_offset_std)
         q, kk, v = draw_frames(spec, layer, 0, max(R, n), device=dev)
         pools.append((q, kk, v))
-    outs = [torch.empty((F, H, D), dtype=torch.bfloat16, device=dev) for _ in range(Ly)]
-    anc_out = torch.empty((n * F, H, D), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((F, H, D), dtype=tdt, device=dev) for _ in range(Ly)]
+    anc_out = torch.empty((n * F, H, D), dtype=tdt, device=dev)
     # per layer, per pool entry: device addresses
     ptrs = []
     for layer in range(Ly):
         q, kk, v = pools[layer]
-        fb = F * H * D * 2
+        fb = F * H * D * esz
         ptrs.append([(ctypes.c_void_p(q.data_ptr() + i * fb), ctypes.c_void_p(kk.data_ptr() + i * fb),
                       ctypes.c_void_p(v.data_ptr() + i * fb)) for i in range(R)])
     optr = [ctypes.c_void_p(o.data_ptr()) for o in outs]
@@ -226,7 +268,10 @@ def main():
     variant += [f"S={S}"] if S != 6 else []
     variant += ["rotary Q/K"] if args.rotary else []
     variant += [f"reset every {W} frames"] if W != T else []
-    variant += [f"{Ly} layers, M={M}, k={k}, T={T}"] if not variant else []
+    variant += [f"key offset N(0, {args.key_offset_std}^2)"] if args.key_offset_std else []
+    variant = [f"{Ly} layers, H={H}, M={M}, k={k}, T={T}, {args.dtype}"] + variant
+    cfg_no = config_workload(args)
+    peak = PEAK_FP32_TFLOPS if f32 else PEAK_BF16_TFLOPS
     result = {
         "metric": METRIC if default_workload(args) else f"GCA frames/s ({', '.join(variant)})",
         "value": round(fps, 2),
@@ -238,21 +283,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1), resident pool of 64 frames per layer)",
+        "dtype": args.dtype,
+        "data": (f"synthetic (seeded N(0,1)"
+                 + (f", per-frame key offset N(0, {args.key_offset_std}^2)" if args.key_offset_std else "")
+                 + f", resident pool of {R} frames per layer)"),
         "config": {"workload": f"GCA direct-mode stream: {Ly} layers, H={H}, D={D}, M={M}+{S}, "
-                               f"n={n}, k={k}, T={T}, keyframe interval {args.keyframe_interval}, bf16"
+                               f"n={n}, k={k}, T={T}, keyframe interval {args.keyframe_interval}, {args.dtype}"
                                + (", rotary Q/K" if args.rotary else "")
+                               + (f", per-frame key offset std {args.key_offset_std}" if args.key_offset_std else "")
                                + (f", reset and anchor init every {W} frames" if W != T else ""),
+                   "config_number": cfg_no or None,
                    "layers": Ly, "heads": H, "head_dim": D, "image_tokens": M,
                    "summary_tokens": S, "n_anchor": n, "k_window": k, "frames": T},
         "roofline": {
             "bound": "mfma",
-            "kernel": "k_attn_bf16",
+            "kernel": "k_attn_f32" if f32 else "k_attn_bf16",
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": read_traffic() if (T, Ly, k, M) == (10000, 12, 64, 500) and default_workload(args) else None,
             "avg_launch_us": round(attn_avg_ms * 1e3, 2),
             "launches": timed_launches,
@@ -262,15 +311,15 @@ def main():
             # the peak assumes 2.4 GHz; the same peak at the clock measured
             # inside the timed launches
             "clock_ghz": round(clock, 3),
-            "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
+            "frac_at_clock": round(achieved / (peak * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
         },
     }
     stack.close()
     del pools
     torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline and default_workload(args):
-        result["cpu_baseline"] = cpu_baseline(args, H, D, M, S, n, k, T, Ly)
+    if not args.no_cpu_baseline and cfg_no:
+        result["cpu_baseline"] = cpu_baseline(args, H, D, M, S, n, k, T, Ly, W, tdt)
     print(json.dumps(result), flush=True)
 
 
@@ -363,11 +412,15 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
-    """Time the fp64 oracle on sampled steps of one layer; extrapolate.
+def cpu_baseline(args, H, D, M, S, n, k, T, Ly, W, tdt):
+    """Time the fp64 oracle on a bounded sample of the workload; extrapolate.
 
-    The oracle's step cost is linear in the key count; time(t) = a + b*keys(t)
-    is fitted to the samples and summed over the stream, times the layers.
+    A stream short enough (the tiny configuration) is timed whole.  Otherwise
+    one layer is timed at sampled steps, smallest key count first, until the
+    budget is spent; the oracle's step cost is linear in the key count, so
+    time(t) = a + b*keys(t) is fitted to the samples and summed over every
+    step of the stream (windows of W frames with an anchor block each), times
+    the layers.
     """
     import numpy as np
     import torch
@@ -392,14 +445,25 @@ def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
         pass
     shp = go.GcaShape(M=M, n=n, k=k, S=S)
     F = M + S
+    scale = 1 / math.sqrt(D)
+    base = {"unit": "frames/s", "cores": int(threads), "kind": "oracle", "cpu": cpu, "blas": blas}
+    if T * Ly <= 256:  # the whole stream, every layer
+        t0 = time.perf_counter()
+        for layer in range(Ly):
+            spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=tdt, seed=0, chunk=16,
+                              key_offset_std=args.key_offset_std)
+            q, kk, v = (x.double().numpy() for x in draw_frames(spec, layer, 0, T))
+            go.stream_online(q, kk, v, shp, scale)
+        secs = time.perf_counter() - t0
+        return dict(base, value=round(T / secs, 6),
+                    sample=f"fp64 numpy oracle over the whole stream ({T} frames x {Ly} layer(s), {secs:.2f} s)")
     R = 16
-    spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=16)
+    spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=tdt, seed=0, chunk=16, key_offset_std=args.key_offset_std)
     q, kk, v = (x.double().numpy() for x in draw_frames(spec, 0, 0, R))
 
     def get_rows(f, rows):
         return kk[f % R][rows], v[f % R][rows]
 
-    scale = 1 / math.sqrt(D)
     samples = []
     budget = args.cpu_seconds
     spent = 0.0
@@ -407,33 +471,33 @@ def cpu_baseline(args, H, D, M, S, n, k, T, Ly):
     go.anchor_init(q[:n].reshape(n * F, H, D), kk[:n].reshape(n * F, H, D), v[:n].reshape(n * F, H, D), scale)
     anchor_s = time.perf_counter() - t_a
     spent += anchor_s
-    for t in (n + k, T // 4, T // 2, T - 1, n + 1):
+    def keys_at(t):  # keys visible at step t: anchors, window, itself, older summaries
+        w = min(k, t - n)
+        return (n + w + 1) * F + S * (t - n - w)
+
+    cand = sorted({min(max(t, n), W - 1) for t in (n + 1, n + k, W // 8, W // 4, W // 2, W - 1)},
+                  key=keys_at)
+    for t in cand:
         if spent > budget and len(samples) >= 2:
             break
-        t = min(max(t, n), T - 1)
         t0 = time.perf_counter()
         go.step(t, q[t % R], get_rows, shp, scale)
         dt = time.perf_counter() - t0
         spent += dt
-        samples.append((go.visible_key_count(t, shp), dt, t))
+        samples.append((keys_at(t), dt, t))
         log(f"cpu oracle step t={t}: {dt:.2f} s")
     keys = np.array([s[0] for s in samples], dtype=float)
     secs = np.array([s[1] for s in samples])
     b, a = np.polyfit(keys, secs, 1) if len(samples) >= 2 else (secs[0] / keys[0], 0.0)
-    all_keys = np.array([go.visible_key_count(t, shp) if t < n + k + 2 else
-                         M * (n + k + 1) + S * (t + 1) for t in range(n, T)], dtype=float)
-    stream_s = Ly * (anchor_s + float(np.sum(a + b * all_keys)))
-    return {
-        "value": round(T / stream_s, 6),
-        "unit": "frames/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "cpu": cpu,
-        "blas": blas,
-        "sample": (f"fp64 numpy oracle, one layer: anchor init + steps t={[s[2] for s in samples]} "
-                   f"({spent:.1f} s); time linear in keys fitted and summed over t={n}..{T - 1}, "
-                   f"x{Ly} layers (extrapolated)"),
-    }
+    steps = [t - w0 for w0 in range(0, T, W) for t in range(w0 + n, min(w0 + W, T))]
+    windows = len(range(0, T, W))
+    all_keys = np.array([keys_at(t) for t in sorted(set(steps))], dtype=float)
+    per_t = dict(zip(sorted(set(steps)), a + b * all_keys))
+    stream_s = Ly * (windows * anchor_s + float(sum(per_t[t] for t in steps)))
+    return dict(base, value=round(T / stream_s, 6),
+                sample=(f"fp64 numpy oracle, one layer: anchor init + steps t={[s[2] for s in samples]} "
+                        f"({spent:.1f} s); time linear in keys fitted and summed over every step of the "
+                        f"stream ({windows} window(s) of {W} frames), x{Ly} layers (extrapolated)"))
 
 
 if __name__ == "__main__":

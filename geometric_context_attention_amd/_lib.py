@@ -23,6 +23,8 @@ GCA_E_BAD_STATE = -2
 GCA_E_OUT_OF_PAGES = -3
 GCA_E_HIP = -4
 GCA_E_UNSUPPORTED = -5
+GCA_ERR_PAGE_OUT_OF_POOL = 1
+GCA_ERR_TABLE_MISMATCH = 2
 
 _DTYPES = {GCA_BF16: torch.bfloat16, GCA_FP32: torch.float32}
 
@@ -88,6 +90,7 @@ _SIGS = {
     "gca_step_keyframe": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_frame_attention": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_set_rotary": (ctypes.c_int, [_VP, _VP]),
+    "gca_debug_set_table_entry": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_int64, _I32, _VP]),
     "gca_profile_enable": (ctypes.c_int, [_VP, _I32]),
     "gca_profile_read": (ctypes.c_int, [_VP, ctypes.POINTER(gca_profile)]),
 }
@@ -221,6 +224,12 @@ def gca_export_state(ctx, layer, stream=None) -> dict:
     out["frame_table"] = ft.reshape(st.max_frames, st.pages_per_frame)
     out["summary_pages"] = sp
     return out
+
+
+def gca_debug_set_table_entry(ctx, layer, table, index, value, stream=None):
+    """Failure injection: overwrite one device frame-table (table 0) or
+    summary-list (table 1) entry."""
+    _check(lib().gca_debug_set_table_entry(ctx, layer, table, index, value, _stream_ptr(stream)))
 
 
 def gca_pool_views(ctx, layer):

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/gca.h"
+
 namespace gca {
 
 constexpr int kPage = 64;        // token slots per page
@@ -39,7 +41,7 @@ enum Ctr : int {
   kCtrTraj = 1,      // frames in trajectory memory
   kCtrSumPages = 2,  // summary pages
   kCtrUsed = 3,      // pages in use
-  kCtrError = 4,     // nonzero: a cache kernel found an inconsistency
+  kCtrError = 4,     // error bits (GCA_ERR_*), sticky until the next reset
   kCtrCount = 8
 };
 

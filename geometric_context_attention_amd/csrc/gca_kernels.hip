@@ -189,7 +189,8 @@ __device__ __forceinline__ int map_page(const AttnArgs& a, int i, int& valid, in
     valid = (i == pl.ppf - 1) ? pl.f_last_valid : kPage;
     pg = fresh_page_ids()[i];
   }
-  if ((unsigned)pg >= (unsigned)a.pool) {
+  if ((unsigned)pg >= (unsigned)a.pool) {  // corrupt table: flag it, read nothing
+    atomicOr(&a.L.ctr[kCtrError], GCA_ERR_PAGE_OUT_OF_POOL);
     valid = 0;
     fj = -1;
     pg = 0;
@@ -222,9 +223,13 @@ __device__ __forceinline__ const_i32p page_source(const AttnArgs& a, int i, int&
 }
 
 // List entry: physical page << 7 | valid slots; an id outside the pool (only
-// possible if the tables are corrupt) becomes page 0 with every slot masked.
+// possible if the tables are corrupt) becomes page 0 with every slot masked,
+// and the layer's error counter records it.
 __device__ __forceinline__ uint32_t page_entry(const AttnArgs& a, int pg, int valid) {
-  if ((unsigned)pg >= (unsigned)a.pool) return 0u;
+  if ((unsigned)pg >= (unsigned)a.pool) {
+    atomicOr(&a.L.ctr[kCtrError], GCA_ERR_PAGE_OUT_OF_POOL);
+    return 0u;
+  }
   return ((uint32_t)pg << 7) | (uint32_t)valid;
 }
 
@@ -1454,6 +1459,7 @@ hipError_t launch_append(const LayerDev& L, const void* k, const void* v, int fr
 hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
   const int grid = a.H * a.qblocks * a.nsplit;
   if (a.batch < 1 || (a.batch > 1 && (a.nsplit != 1 || a.pl.fresh_cnt != a.pl.ppf))) return hipErrorInvalidValue;
+  if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr)) return hipErrorInvalidValue;
   const dim3 g3(grid, a.batch);
   // the bf16 kernel keeps its split's page list in LDS (the split count is
   // chosen so it always fits; checked here before anything is launched)
@@ -1481,6 +1487,7 @@ hipError_t launch_frame_wsplit(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_merge_evict(const AttnArgs& a, const EvictPlan* ev, bool f32, hipStream_t st) {
+  if (a.nsplit > 1 && (a.part_o == nullptr || a.part_ml == nullptr)) return hipErrorInvalidValue;
   const int rowblocks = a.nsplit > 1 ? (a.Lq + 15) / 16 : 0;
   const int mheads = a.nsplit > 1 ? a.H : 0;
   const int eblocks = ev != nullptr ? a.H : 0;

@@ -93,6 +93,10 @@ int validate(const gca_config* c, std::string& why) {
   if ((int64_t)c->n_anchor * F > (1 << 24)) { why = "anchor block too large"; return GCA_E_INVALID_ARG; }
   const int64_t ppf = cdiv(F, kPage);
   if (ppf > kMaxFramePages) { why = "frames of more than 2048 tokens are not supported"; return GCA_E_UNSUPPORTED; }
+  if (c->pool_pages != 0 && c->pool_pages < (int64_t)c->n_anchor * ppf) {
+    why = "pool_pages is smaller than the anchor block";
+    return GCA_E_INVALID_ARG;
+  }
   if ((int64_t)c->max_frames * ppf > (1LL << 30)) { why = "max_frames too large"; return GCA_E_INVALID_ARG; }
   return GCA_OK;
 }
@@ -129,7 +133,10 @@ void make_geometry(const gca_config& c, Geometry& g) {
   const int64_t peak = peak_pages(c, g.ppf);
   g.pool = c.pool_pages > 0 ? c.pool_pages : (int)peak;
   g.words = (int)cdiv(g.pool, 32);
-  const int64_t traj_max = std::max<int64_t>(0, keyframes_before(c, c.max_frames) - c.k_window);
+  // The summary list is sized for every frame being cached (gca_step_keyframe
+  // lets the caller cache more frames than the keyframe schedule); only the
+  // pool is sized for the schedule.
+  const int64_t traj_max = std::max<int64_t>(0, (int64_t)c.max_frames - c.n_anchor - c.k_window);
   g.max_sum_pages = (int)std::max<int64_t>(1, cdiv(traj_max * c.summary_tokens, kPage));
   g.ftab_entries = (int64_t)c.max_frames * g.ppf;
   g.eb = c.dtype == GCA_FP32 ? 4 : 2;
@@ -145,7 +152,9 @@ void make_geometry(const gca_config& c, Geometry& g) {
   for (int64_t L : lq) {
     const int qb = (int)cdiv(L, qr);
     const int64_t lq_pad = cdiv(L, kQBlock) * kQBlock;
-    const int s = choose_splits(c, qb, g.pool);  // no step sees more pages than the pool holds
+    // no step sees more pages than the pool holds, and the pool holds the
+    // anchor block (validate), so also a lone frame of intra-frame attention
+    const int s = choose_splits(c, qb, std::max<int64_t>(g.pool, (int64_t)c.n_anchor * g.ppf));
     if (s > 1) {
       po = std::max(po, (size_t)c.num_heads * s * lq_pad * kHeadDim * (c.dtype == GCA_FP32 ? 4 : 2));
       pml = std::max(pml, (size_t)c.num_heads * s * lq_pad * 8);
@@ -356,8 +365,6 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
   Geometry g;
   make_geometry(*cfg, g);
   if (bytes < g.total) return fail(GCA_E_INVALID_ARG, "workspace too small: need " + std::to_string(g.total) + " bytes");
-  if (cfg->pool_pages == 0 && g.pool < (int64_t)cfg->n_anchor * g.ppf)
-    return fail(GCA_E_INVALID_ARG, "pool smaller than the anchor block");
   gca_ctx* c = new gca_ctx();
   c->cfg = *cfg;
   c->g = g;
@@ -466,6 +473,8 @@ int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const voi
   const int new_sum = evict ? (int)(cdiv((int64_t)S * (hs.traj + 1), kPage) - nsp) : 0;
   if ((int64_t)hs.used + g.ppf + new_sum > g.pool)
     return fail(GCA_E_OUT_OF_PAGES, "page pool exhausted at frame " + std::to_string(t));
+  if (nsp + new_sum > g.max_sum_pages)  // cannot happen with the list sized for every frame
+    return fail(GCA_E_OUT_OF_PAGES, "summary page list full at frame " + std::to_string(t));
   hipStream_t st = (hipStream_t)stream;
   // pages of frame t (lowest free first; a non-keyframe gives them back at
   // the end of the step); then, if a keyframe leaves the window, a new
@@ -641,17 +650,46 @@ int gca_export_state(gca_ctx* c, int32_t layer, gca_state_host* dst, void* strea
     e = hipMemcpyAsync(dst->frame_table, d.ftab, (size_t)c->g.ftab_entries * 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess && dst->summary_pages)
     e = hipMemcpyAsync(dst->summary_pages, d.slist, (size_t)c->g.max_sum_pages * 4, hipMemcpyDeviceToHost, st);
+  // the device tables, for the comparison with the host's record
+  const LayerHost& hs = c->host[layer];
+  std::vector<uint32_t> bits(hs.bits.size());
+  std::vector<int32_t> ftab(hs.ftab.size()), slist(hs.slist.size());
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(bits.data(), d.bitmap, bits.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ftab.data(), d.ftab, ftab.size() * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(slist.data(), d.slist, slist.size() * 4, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return hip_fail(e, "export_state copy");
+  const int64_t sum_pages = cdiv((int64_t)c->cfg.summary_tokens * hs.traj, kPage);
+  const bool same = bits == hs.bits && ftab == hs.ftab && slist == hs.slist &&
+                    ctr[kCtrFrames] == hs.frames && ctr[kCtrTraj] == hs.traj &&
+                    ctr[kCtrSumPages] == sum_pages && ctr[kCtrUsed] == hs.used;
   dst->frames_appended = ctr[kCtrFrames];
   dst->n_traj = ctr[kCtrTraj];
   dst->n_summary_pages = ctr[kCtrSumPages];
   dst->used_pages = ctr[kCtrUsed];
-  dst->device_error = ctr[kCtrError];
+  dst->device_error = ctr[kCtrError] | (same ? 0 : GCA_ERR_TABLE_MISMATCH);
   dst->pool_pages = c->g.pool;
   dst->pages_per_frame = c->g.ppf;
   dst->max_frames = c->cfg.max_frames;
   dst->max_summary_pages = c->g.max_sum_pages;
+  return GCA_OK;
+}
+
+int gca_debug_set_table_entry(gca_ctx* c, int32_t layer, int32_t table, int64_t index,
+                              int32_t value, void* stream) {
+  int rc = check_ctx_layer(c, layer);
+  if (rc != GCA_OK) return rc;
+  const int64_t n = table == 0 ? c->g.ftab_entries : table == 1 ? c->g.max_sum_pages : -1;
+  if (n < 0) return fail(GCA_E_INVALID_ARG, "table must be 0 (frame table) or 1 (summary list)");
+  if (index < 0 || index >= n) return fail(GCA_E_INVALID_ARG, "table index out of range");
+  int32_t* dst = (table == 0 ? c->dev[layer].ftab : c->dev[layer].slist) + index;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(dst, &value, 4, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);  // `value` lives on this stack frame
+  if (e != hipSuccess) return hip_fail(e, "debug table write");
   return GCA_OK;
 }
 

@@ -180,6 +180,18 @@ typedef struct {
 int gca_plan(const gca_config* cfg, int32_t t, gca_plan_info* out);
 
 /* ---- inspection (tests) and profiling ---- */
+
+/* Bits of gca_state_host.device_error. */
+enum {
+  /* a kernel met a page id outside the pool in the frame table or the
+     summary list (it read nothing there and masked every slot of that page);
+     set on the device, kept until gca_reset */
+  GCA_ERR_PAGE_OUT_OF_POOL = 1,
+  /* gca_export_state found the device's frame table, summary list, bitmap or
+     counters different from the host's record of every decision it made */
+  GCA_ERR_TABLE_MISMATCH = 2
+};
+
 typedef struct {
   int32_t frames_appended; /* frames in the cache's frame table so far (anchors, then
                               keyframes); equals the next frame index when every frame
@@ -191,15 +203,29 @@ typedef struct {
   int32_t pages_per_frame;
   int32_t max_frames;
   int32_t max_summary_pages;
-  int32_t device_error;    /* nonzero if a cache kernel found an inconsistency */
+  int32_t device_error;    /* GCA_ERR_* bits; 0 when the device tables are consistent */
   uint32_t* used_bitmap;   /* host buffer [ceil(pool_pages/32)] or NULL */
   int32_t* frame_table;    /* host buffer [max_frames * pages_per_frame] or NULL; -1 = none */
   int32_t* summary_pages;  /* host buffer [max_summary_pages] or NULL */
 } gca_state_host;
 
 /* Copy `layer`'s page-table state (counters from device memory, plus the
- * arrays whose pointers are non-NULL) to the host.  Synchronises `stream`. */
+ * arrays whose pointers are non-NULL) to the host, and check it: the frame
+ * table, summary list, bitmap and counters the kernels wrote are compared
+ * with the host's own record of every page decision (a difference sets
+ * GCA_ERR_TABLE_MISMATCH), and the kernels' error bits are added.
+ * Synchronises `stream`. */
 int gca_export_state(gca_ctx* ctx, int32_t layer, gca_state_host* dst, void* stream);
+
+/* Failure injection for tests (the consistency check above must catch a
+ * corrupted table): write `value` into entry `index` of `layer`'s device frame
+ * table (table 0, [max_frames * pages_per_frame] entries) or summary list
+ * (table 1, [max_summary_pages] entries), ordered on `stream`, leaving the
+ * host's record alone.  An index out of range is GCA_E_INVALID_ARG.  A value
+ * outside [0, pool_pages) is never dereferenced: attention masks that page and
+ * sets GCA_ERR_PAGE_OUT_OF_POOL.  gca_reset clears the tables and the bits. */
+int gca_debug_set_table_entry(gca_ctx* ctx, int32_t layer, int32_t table, int64_t index,
+                              int32_t value, void* stream);
 
 /* Device addresses of `layer`'s K and V page pools and the byte size of one
  * page.  Page p of K holds [H][P][D] (slot s of head h at row s); page p of V

@@ -51,6 +51,17 @@ def test_invalid_configs_are_rejected(bad, code):
     assert ei.value.code == code
 
 
+def test_pool_smaller_than_the_anchor_block_is_rejected():
+    """An explicit pool must hold the n anchor frames (3 frames x 2 pages here);
+    a smaller one is refused before any workspace is sized."""
+    cfg = _cfg(image_tokens=100, pool_pages=5)
+    assert G.lib().gca_workspace_bytes(ctypes.byref(cfg)) == 0
+    with pytest.raises(G.GcaError) as ei:
+        G.gca_plan(cfg, 5)
+    assert ei.value.code == G.GCA_E_INVALID_ARG
+    assert G.gca_workspace_bytes(_cfg(image_tokens=100, pool_pages=6)) > 0
+
+
 def test_workspace_grows_with_layers_and_pool():
     a = G.gca_workspace_bytes(_cfg())
     b = G.gca_workspace_bytes(_cfg(num_layers=3))

@@ -25,32 +25,54 @@ D, C = 64, 32
 
 
 def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_offset_std=0.0,
-              heads=None, row_stride=1, bytes_at=(), interval=1, rotary=False, S=6):
+              heads=None, row_stride=1, bytes_at=(), interval=1, rotary=False, S=6,
+              num_layers=1, check_layers=(0,), sharpen_at=()):
+    """Stream T frames through a stack of num_layers layers (stack layer i
+    draws the seeds of layer `layer + i`), comparing the outputs of
+    check_layers with the oracle at the frames in `samples` and their cache
+    state at `state_at` (cached bytes too at `bytes_at`).  heads: the heads
+    compared, or a function of the frame giving them.  At the frames in
+    sharpen_at the queries are scaled by 4 (the cache does not depend on Q),
+    which peaks the softmax so that the max-abs gate has teeth."""
     F = M + S
     Tw = window_len or T
     spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=C,
                       key_offset_std=key_offset_std)
-    cfg = G.make_config(num_heads=H, image_tokens=M, summary_tokens=S, n_anchor=n, k_window=k,
-                        max_frames=Tw, dtype=G.GCA_BF16, keyframe_interval=interval)
+    cfg = G.make_config(num_layers=num_layers, num_heads=H, image_tokens=M, summary_tokens=S,
+                        n_anchor=n, k_window=k, max_frames=Tw, dtype=G.GCA_BF16,
+                        keyframe_interval=interval)
     stack = G.GcaStack(cfg)
     pool = G.gca_plan(cfg, 0)["pool_pages"]
-    pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=pool, max_frames=Tw, m=interval)
     shp = GcaShape(M=M, n=n, k=k, S=S, m=interval)
     scale = 1 / math.sqrt(D)
-    hs = list(range(H)) if heads is None else list(heads)
+
+    def heads_at(g):
+        if heads is None:
+            return list(range(H))
+        return list(heads(g)) if callable(heads) else list(heads)
+
     keep_chunks = (min(k * interval, Tw) + 1) // C + 2  # the window spans k keyframes
-    keep = {}
-    sum_k = torch.empty((T, S, H, D), dtype=torch.bfloat16)
-    sum_v = torch.empty((T, S, H, D), dtype=torch.bfloat16)
+    checked_layers = list(check_layers)
+
+    class Lay:  # what the oracle needs of one checked layer
+        def __init__(self):
+            self.pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=pool, max_frames=Tw, m=interval)
+            self.keep = {}
+            self.sum_k = torch.empty((T, S, H, D), dtype=torch.bfloat16)
+            self.sum_v = torch.empty((T, S, H, D), dtype=torch.bfloat16)
+            self.anc = None  # (q, k, v, angles) of the current window's anchor frames, device
+            self.checked = 0
+
+    lays = {i: Lay() for i in checked_layers}
+    cur = {}  # stack layer -> (q, k, v) of the current chunk (unchecked layers)
     # Rotary angles use the frame index as time (synth recipe); summary rows
     # sit at patch (0, 0), so their angles depend on the frame alone.
     tab_sum = rotary_table(0, T, S, S) if rotary else None  # [T, S, D/2, 2]
     tab_sum_d = tab_sum.cuda() if rotary else None
-    anc = None  # (q, k, v, angles) of the current window's anchor frames, device
-    checked = 0
+    tab_cur = None
 
-    def frame(g):
-        q, kk, v, tab = keep[g // C]
+    def frame(ly, g):
+        q, kk, v, tab = ly.keep[g // C]
         i = g % C
         return q[i], kk[i], v[i], (tab[i] if rotary else None)
 
@@ -59,25 +81,26 @@ def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_o
         x = to64(x)
         return go.rotary(x, to64(tab)) if rotary else x
 
-    def provider(w0, t):
+    def provider(ly, w0, hs):
         def get_rows(f, rows):
             rows = np.asarray(rows)
             g = w0 + f
             ri = torch.as_tensor(rows)
             if rows.max() >= S:  # a full frame: anchor, window keyframe or the current frame
                 if f < n:
-                    kk, v, tab = anc[1][f], anc[2][f], (anc[3][f] if rotary else None)
+                    kk, v, tab = ly.anc[1][f], ly.anc[2][f], (ly.anc[3][f] if rotary else None)
                 else:
-                    assert g // C in keep, f"frame {g} left the kept chunks"
-                    _, kk, v, tab = frame(g)
+                    assert g // C in ly.keep, f"frame {g} left the kept chunks"
+                    _, kk, v, tab = frame(ly, g)
                 rd = ri.to(kk.device)
-                kr = rot64(kk[rd], tab[rd] if rotary else None)
-                return kr[:, hs], to64(v[rd])[:, hs]
-            kr = rot64(sum_k[g, ri], tab_sum[g, ri] if rotary else None)
-            return kr[:, hs], to64(sum_v[g, ri])[:, hs]
+                hd = torch.as_tensor(hs, device=kk.device)
+                kr = rot64(kk[rd][:, hd], tab[rd] if rotary else None)
+                return kr, to64(v[rd][:, hd])
+            kr = rot64(ly.sum_k[g, ri][:, hs], tab_sum[g, ri] if rotary else None)
+            return kr, to64(ly.sum_v[g, ri][:, hs])
         return get_rows
 
-    def rows_batch(w0):
+    def rows_batch(ly, w0):
         def fn(fr, rw):
             out_k = torch.empty((len(fr), H, D), dtype=torch.bfloat16, device="cuda")
             out_v = torch.empty_like(out_k)
@@ -87,16 +110,16 @@ def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_o
             gi = torch.as_tensor(w0 + fr[idx])
             ri = torch.as_tensor(rw[idx])
             di = torch.as_tensor(idx, device="cuda")
-            out_k[di] = sum_k[gi, ri].cuda()
-            out_v[di] = sum_v[gi, ri].cuda()
+            out_k[di] = ly.sum_k[gi, ri].cuda()
+            out_v[di] = ly.sum_v[gi, ri].cuda()
             if rotary:
                 out_t[di] = tab_sum_d[gi.cuda(), ri.cuda()]
             for f in np.unique(fr[~summ]):
                 sel = np.nonzero((fr == f) & ~summ)[0]
                 if f < n:
-                    kk, v, tab = anc[1][f], anc[2][f], (anc[3][f] if rotary else None)
+                    kk, v, tab = ly.anc[1][f], ly.anc[2][f], (ly.anc[3][f] if rotary else None)
                 else:
-                    _, kk, v, tab = frame(w0 + f)
+                    _, kk, v, tab = frame(ly, w0 + f)
                 r = torch.as_tensor(rw[sel], device="cuda")
                 ds = torch.as_tensor(sel, device="cuda")
                 out_k[ds] = kk[r]
@@ -108,62 +131,90 @@ def _fullsize(M, n, k, T, H, layer, samples, state_at=(), window_len=None, key_o
             return out_k, out_v
         return fn
 
+    def frame_any(i, g):
+        """q, k, v, angles of frame g for stack layer i."""
+        if i in lays:
+            return frame(lays[i], g)
+        q, kk, v = cur[i]
+        j = g % C
+        return q[j], kk[j], v[j], (tab_cur[j] if rotary else None)
+
     for g in range(T):
         if g % C == 0:
             c = g // C
-            q_c, k_c, v_c = draw_chunk(spec, layer, c, device="cuda")
-            tab_c = rotary_table(c * C, C, F, S).cuda() if rotary else None  # [C, F, D/2, 2]
-            keep[c] = (q_c, k_c, v_c, tab_c)
+            tab_cur = rotary_table(c * C, C, F, S).cuda() if rotary else None  # [C, F, D/2, 2]
             hi = min(C, T - g)
-            sum_k[g:g + hi] = k_c[:hi, :S].cpu()
-            sum_v[g:g + hi] = v_c[:hi, :S].cpu()
-            for old in [x for x in keep if x < c - keep_chunks]:
-                del keep[old]
+            for i in range(num_layers):
+                q_c, k_c, v_c = draw_chunk(spec, layer + i, c, device="cuda")
+                if i in lays:
+                    ly = lays[i]
+                    ly.keep[c] = (q_c, k_c, v_c, tab_cur)
+                    ly.sum_k[g:g + hi] = k_c[:hi, :S].cpu()
+                    ly.sum_v[g:g + hi] = v_c[:hi, :S].cpu()
+                    for old in [x for x in ly.keep if x < c - keep_chunks]:
+                        del ly.keep[old]
+                else:
+                    cur[i] = (q_c, k_c, v_c)
         t = g % Tw
         w0 = g - t
         if t == 0 and g > 0:
             stack.reset()
-            pm.reset()
+            for ly in lays.values():
+                ly.pm.reset()
         if t < n - 1:
             continue
-        if t == n - 1:
-            fa = [frame(w0 + f) for f in range(n)]
-            qa = torch.stack([x[0] for x in fa]).reshape(n * F, H, D)
-            ka = torch.stack([x[1] for x in fa])
-            va = torch.stack([x[2] for x in fa])
-            ta = torch.stack([x[3] for x in fa]) if rotary else None  # kept alive with anc
-            anc = (qa, ka, va, ta)
-            if rotary:
-                G.gca_set_rotary(stack.ctx, ta.reshape(n * F, D // 2, 2))
-            out, lse = stack.anchor_init(0, qa, ka.reshape(n * F, H, D), va.reshape(n * F, H, D))
-            pm.anchor_init()
-            if g in samples:
-                tq = ta.reshape(n * F, D // 2, 2) if rotary else None
-                ref, lref = go.anchor_init(rot64(qa, tq)[:, hs], rot64(ka.reshape(n * F, H, D), tq)[:, hs],
-                                           to64(va.reshape(n * F, H, D))[:, hs], scale)
-                check_outputs(out[:, hs], ref, lse[hs], lref, "bf16", f"anchor init at frame {g}")
-                checked += 1
-        else:
-            q, kk, v, tab = frame(g)
-            if rotary:
-                G.gca_set_rotary(stack.ctx, tab)
-            out, lse = stack.step(0, q, kk, v)
-            pm.step(t)
-            if g in samples:
-                rows = np.arange(0, F, row_stride)
-                rd = torch.as_tensor(rows, device="cuda")
-                qr = rot64(q[rd], tab[rd] if rotary else None)
-                ref, lref = go.step(t, qr[:, hs], provider(w0, t), shp, scale)
-                ma, rel = check_outputs(out[rd][:, hs], ref, lse[hs][:, rd], lref,
-                                        "bf16", f"frame {g} (step {t})")
-                say(f"  frame {g}: keys {go.visible_key_count(t, shp)}, max-abs {ma:.2e}, rel {rel:.2e}")
-                checked += 1
-        if g in state_at:
-            check_state(stack, 0, pm, rows_of_batch=rows_batch(w0) if g in bytes_at else None)
+        hs = heads_at(g)
+        for i in range(num_layers):
+            ly = lays.get(i)
+            if t == n - 1:
+                fa = [frame_any(i, w0 + f) for f in range(n)]
+                qa = torch.stack([x[0] for x in fa]).reshape(n * F, H, D)
+                ka = torch.stack([x[1] for x in fa])
+                va = torch.stack([x[2] for x in fa])
+                ta = torch.stack([x[3] for x in fa]) if rotary else None  # kept alive with anc
+                if ly is not None:
+                    ly.anc = (qa, ka, va, ta)
+                if rotary:
+                    G.gca_set_rotary(stack.ctx, ta.reshape(n * F, D // 2, 2))
+                out, lse = stack.anchor_init(i, qa, ka.reshape(n * F, H, D), va.reshape(n * F, H, D))
+                if ly is None:
+                    continue
+                ly.pm.anchor_init()
+                if g in samples:
+                    tq = ta.reshape(n * F, D // 2, 2) if rotary else None
+                    ref, lref = go.anchor_init(rot64(qa, tq)[:, hs], rot64(ka.reshape(n * F, H, D), tq)[:, hs],
+                                               to64(va.reshape(n * F, H, D))[:, hs], scale)
+                    check_outputs(out[:, hs], ref, lse[hs], lref, "bf16", f"layer {i} anchor init at frame {g}")
+                    ly.checked += 1
+            else:
+                q, kk, v, tab = frame_any(i, g)
+                if g in sharpen_at:
+                    q = (q.float() * 4.0).to(q.dtype)
+                if rotary:
+                    G.gca_set_rotary(stack.ctx, tab)
+                out, lse = stack.step(i, q, kk, v, want_lse=ly is not None)
+                if ly is None:
+                    continue
+                ly.pm.step(t)
+                if g in samples:
+                    rows = np.arange(0, F, row_stride)
+                    rd = torch.as_tensor(rows, device="cuda")
+                    hd = torch.as_tensor(hs, device="cuda")
+                    qr = rot64(q[rd][:, hd], tab[rd] if rotary else None)
+                    ref, lref = go.step(t, qr, provider(ly, w0, hs), shp, scale)
+                    what = f"layer {i} frame {g} (step {t})" + (", Q x4" if g in sharpen_at else "")
+                    ma, rel = check_outputs(out[rd][:, hd], ref, lse[hd][:, rd], lref, "bf16", what)
+                    say(f"  {what}: keys {go.visible_key_count(t, shp)}, heads {hs[0]}..{hs[-1]}, "
+                        f"max-abs {ma:.2e}, rel {rel:.2e}")
+                    ly.checked += 1
+            if ly is not None and g in state_at:
+                check_state(stack, i, ly.pm, rows_of_batch=rows_batch(ly, w0) if g in bytes_at else None)
     if rotary:
         G.gca_set_rotary(stack.ctx, None)
-    assert checked == len(samples)
+    for i, ly in lays.items():
+        assert ly.checked == len(samples), f"layer {i}: {ly.checked} of {len(samples)} samples checked"
     stack.close()
+
 
 def test_paper_shape_one_layer_k16_correlated_keys():
     """M=500+6, 16 heads, n=3, k=16, T=10000, per-frame key offsets N(0, 0.5^2);
@@ -173,10 +224,16 @@ def test_paper_shape_one_layer_k16_correlated_keys():
               state_at={2, 3, 19, 20, 1000, T - 1}, bytes_at={20, T - 1}, key_offset_std=0.5)
 
 
-def test_direct_mode_layer_k64():
-    """The benchmark's stack shape (k=64), layer index 11's seeds, T=10000."""
+def test_direct_mode_stack_12_layers():
+    """The benchmark's own context: a 12-layer stack (M=500+6, 16 heads, n=3,
+    k=64, T=10000, bf16, the 4.4 GiB workspace), every layer stepped every
+    frame in the benchmark's launch configuration.  Layers 0, 5 and 11 are
+    compared with the oracle on all rows and all heads, once with the
+    queries scaled by 4 at 94k keys; layer 11's state and cached bytes are
+    bit-exact at the end."""
     T = 10000
-    _fullsize(500, 3, 64, T, 16, layer=11, samples={3, 66, 67, 68, 5000, T - 1},
+    _fullsize(500, 3, 64, T, 16, layer=0, num_layers=12, check_layers=(0, 5, 11),
+              samples={2, 3, 66, 67, 68, 5000, T - 2, T - 1}, sharpen_at={T - 2},
               state_at={67, 68, T - 1}, bytes_at={T - 1})
 
 
@@ -190,9 +247,13 @@ def test_dense_grid_with_window_resets():
 
 def test_full_causal_cache():
     """k >= T (every frame keeps all 506 tokens), T=2000: 1,012,000 keys at the
-    last step; sampled heads and rows there."""
+    last step.  Four heads per sample, rotating so that the five samples
+    cover all 16 heads; every 4th row."""
     T = 2000
-    _fullsize(500, 3, T, T, 16, layer=0, samples={3, 1000, T - 1}, heads=(0, 7, 15), row_stride=4,
+    samples = sorted({3, 500, 1000, 1500, T - 1})
+    order = {g: i for i, g in enumerate(samples)}
+    _fullsize(500, 3, T, T, 16, layer=0, samples=set(samples),
+              heads=lambda g: [(4 * order.get(g, 0) + j) % 16 for j in range(4)], row_stride=4,
               state_at={1000, T - 1}, bytes_at={1000})
 
 

@@ -23,13 +23,14 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 
 def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scale=1.0,
-                state_every=1, check_bytes=True, key_offset_std=0.0, interval=1, chosen=None):
+                state_every=1, check_bytes=True, key_offset_std=0.0, interval=1, chosen=None,
+                pool_pages=0):
     """Stream T frames through every layer; compare each step with the oracle."""
     gdt, tdt = DT[mode]
     F = M + S
     cfg = G.make_config(num_layers=layers, num_heads=H, image_tokens=M, summary_tokens=S,
                         n_anchor=n, k_window=k, max_frames=T, dtype=gdt, max_splits=max_splits,
-                        keyframe_interval=interval)
+                        keyframe_interval=interval, pool_pages=pool_pages)
     stack = G.GcaStack(cfg)
     shp = GcaShape(M=M, n=n, k=k, S=S, m=interval, kf=chosen)
     scale = 1 / math.sqrt(64)
@@ -240,3 +241,60 @@ def test_bf16_caller_chosen_keyframes():
     rng = np.random.default_rng(5)
     chosen = frozenset(int(t) for t in range(3, 60) if rng.random() < 0.4)
     _run_stream("bf16", M=120, n=3, k=4, T=60, H=4, chosen=chosen, state_every=3)
+
+
+def test_caller_caches_more_frames_than_the_schedule():
+    """Keyframe interval 4 sizes the pool for one frame in four; with a pool
+    large enough the caller may still cache every frame (gca_step_keyframe),
+    and the summary list holds them all: state bit-exact, outputs green."""
+    chosen = frozenset(range(3, 60))
+    _run_stream("bf16", M=40, n=3, k=4, T=60, H=2, interval=4, chosen=chosen, pool_pages=64,
+                state_every=4)
+
+
+def test_corrupted_tables_are_flagged():
+    """Failure injection: a frame-table entry overwritten with another in-pool
+    page is reported by gca_export_state (the device tables no longer match
+    the host's record); an entry outside the pool is masked by attention,
+    which flags it on the device.  gca_reset clears both."""
+    H, M, n, k, T = 2, 100, 3, 4, 12
+    F = M + 6
+    cfg = G.make_config(num_heads=H, image_tokens=M, n_anchor=n, k_window=k, max_frames=T,
+                        dtype=G.GCA_BF16, max_splits=1)
+    st = G.GcaStack(cfg)
+    spec = StreamSpec(H=H, D=64, M=M, dtype=torch.bfloat16, seed=3, chunk=16)
+    q, kx, v = (t.cuda() for t in draw_frames(spec, 0, 0, T))
+    rows = n * F
+    st.anchor_init(0, q[:n].reshape(rows, H, 64), kx[:n].reshape(rows, H, 64), v[:n].reshape(rows, H, 64))
+    for t in range(n, 6):
+        st.step(0, q[t], kx[t], v[t])
+    s0 = st.export_state(0)
+    assert s0["device_error"] == 0
+    ft = s0["frame_table"]
+    ppf = s0["pages_per_frame"]
+    pool = s0["pool_pages"]
+    # entry 1 of anchor frame 1 (not the first page of the split) -> another in-pool page
+    idx = ppf + 1
+    true_pg = int(ft.reshape(-1)[idx])
+    other = (true_pg + 1) % pool
+    G.gca_debug_set_table_entry(st.ctx, 0, 0, idx, other)
+    s1 = st.export_state(0)
+    assert s1["device_error"] == G.GCA_ERR_TABLE_MISMATCH
+    assert int(s1["frame_table"].reshape(-1)[idx]) == other
+    G.gca_debug_set_table_entry(st.ctx, 0, 0, idx, true_pg)  # restored: consistent again
+    assert st.export_state(0)["device_error"] == 0
+    # an id outside the pool: the next step masks that page and flags it
+    G.gca_debug_set_table_entry(st.ctx, 0, 0, idx, pool + 7)
+    out, _ = st.step(0, q[6], kx[6], v[6])
+    torch.cuda.synchronize()
+    s2 = st.export_state(0)
+    assert s2["device_error"] & G.GCA_ERR_PAGE_OUT_OF_POOL
+    assert s2["device_error"] & G.GCA_ERR_TABLE_MISMATCH
+    # out-of-range indices and unknown tables are refused on the host
+    for table, index in ((0, -1), (0, T * ppf), (1, 10 ** 6), (2, 0)):
+        with pytest.raises(G.GcaError) as e:
+            G.gca_debug_set_table_entry(st.ctx, 0, table, index, 0)
+        assert e.value.code == G.GCA_E_INVALID_ARG
+    st.reset()
+    assert st.export_state(0)["device_error"] == 0
+    st.close()
