@@ -88,6 +88,7 @@ _SIGS = {
     "gca_pool_views": (ctypes.c_int, [_VP, _I32, ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(ctypes.c_size_t)]),
     "gca_step_keyframe": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
+    "gca_step_noalloc": (ctypes.c_int, [_VP, _I32, _VP, _VP, _VP, _VP, _VP, _VP]),
     "gca_frame_attention": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I32, _VP]),
     "gca_set_rotary": (ctypes.c_int, [_VP, _VP]),
     "gca_debug_set_table_entry": (ctypes.c_int, [_VP, _I32, _I32, ctypes.c_int64, _I32, _VP]),
@@ -181,6 +182,12 @@ def gca_step_keyframe(ctx, layer, q, k, v, out, lse=None, append=True, stream=No
     _check(lib().gca_step_keyframe(ctx, layer, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
                                    _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
                                    1 if append else 0, _stream_ptr(stream)))
+
+
+def gca_step_noalloc(ctx, layer, q, k, v, out, lse=None, stream=None):
+    _check(lib().gca_step_noalloc(ctx, layer, _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
+                                  _ptr(out, name="out"), _ptr(lse, torch.float32, name="lse"),
+                                  _stream_ptr(stream)))
 
 
 def gca_frame_attention(ctx, q, k, v, out, lse=None, frames=1, stream=None):

@@ -123,6 +123,13 @@ struct EvictPlan {
   int32_t new_index;
 };
 
+// Split-K scratch of gca_step_noalloc: a static device array of this many
+// bytes (one per GPU, held until the process ends), shared by every call on
+// that GPU.  static_scratch_address gives its device address on the current
+// device (looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch_address(void** out);
+
 // Launch wrappers (gca_kernels.hip).  All return hipGetLastError() after launch.
 hipError_t launch_reset(const LayerDev& L, int pool_words, int ftab_entries, int slist_entries,
                         hipStream_t st);

@@ -19,7 +19,9 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 #include "gca_internal.h"
 
@@ -1425,6 +1427,34 @@ __global__ __launch_bounds__(256) void k_merge_evict(AttnArgs a, EvictPlan e, in
     using T = typename std::conditional<kF32, float, uint16_t>::type;
     evict_block<T>(a.L, e, b - nmerge, a.H);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Static split-K scratch (gca_step_noalloc)
+// ---------------------------------------------------------------------------
+
+// The split partials of gca_step_noalloc live here instead of in the
+// caller's workspace.  Host code never uses this name as an address: each
+// device's copy sits at its own address, which static_scratch_address looks
+// up once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<void*> addr;  // per device
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

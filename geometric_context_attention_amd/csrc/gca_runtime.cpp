@@ -235,6 +235,7 @@ struct gca_ctx {
   std::vector<LayerHost> host;
   void* part_o = nullptr;
   float2* part_ml = nullptr;
+  void* static_scratch = nullptr;       // this device's static split-K scratch (gca_step_noalloc)
   unsigned long long* clock = nullptr;  // [2] device: shader cycles, reference ticks
   LayerDev scratch{};                   // ppf K/V pages for frame attention (pools only)
   const float2* rope = nullptr;         // rotary table of the next calls (gca_set_rotary)
@@ -267,13 +268,24 @@ int harvest(gca_ctx* c, EventPair& e) {
   return GCA_OK;
 }
 
+// Bytes of split-K partials (O, then the (m, l) pairs at the next 256-byte
+// boundary) of an attention launch with `nsplit` splits over Lq query rows.
+size_t partial_bytes(const gca_ctx* c, int Lq, int nsplit, size_t* ml_offset) {
+  const size_t lq_pad = (size_t)cdiv(Lq, kQBlock) * kQBlock;
+  const size_t o = align256((size_t)c->cfg.num_heads * nsplit * lq_pad * kHeadDim * c->g.eb);
+  if (ml_offset) *ml_offset = o;
+  return nsplit > 1 ? o + (size_t)c->cfg.num_heads * nsplit * lq_pad * sizeof(float2) : 0;
+}
+
 // Attention over the page list `pl` for `Lq` query rows (appending the frame
 // `fresh_frame` from k/v when pl.fresh_cnt > 0), then the merge of the key
-// splits and the eviction `ev` (if any) in a second launch.
+// splits and the eviction `ev` (if any) in a second launch.  With
+// static_partials the split partials go to the static scratch array (the
+// caller has checked that they fit) instead of the workspace.
 int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const void* v,
                      void* out, float* lse, int Lq, const PageList& pl, const FramePages& fresh,
                      int fresh_frame, const EvictPlan* ev, int64_t keys, hipStream_t st,
-                     bool use_scratch = false, int batch = 1) {
+                     bool use_scratch = false, int batch = 1, bool static_partials = false) {
   const gca_config& cfg = c->cfg;
   AttnArgs a{};
   a.q = q;
@@ -304,6 +316,13 @@ int run_step_kernels(gca_ctx* c, int layer, const void* q, const void* k, const 
   a.lse = lse;
   a.part_o = c->part_o;
   a.part_ml = c->part_ml;
+  if (static_partials) {
+    size_t ml_off = 0;
+    if (partial_bytes(c, Lq, a.nsplit, &ml_off) > kStaticScratchBytes)
+      return fail(GCA_E_INVALID_ARG, "split partials exceed the static scratch");  // checked by the caller
+    a.part_o = c->static_scratch;
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(c->static_scratch) + ml_off);
+  }
   a.Lq_pad = (int)(cdiv(Lq, kQBlock) * kQBlock);
   a.pool = use_scratch ? c->g.ppf : c->g.pool;
   a.rope = c->rope;
@@ -392,6 +411,11 @@ int gca_create(const gca_config* cfg, void* dev_workspace, size_t bytes, void* s
   c->clock = (unsigned long long*)(tail + g.part_o_bytes + g.part_ml_bytes);
   c->scratch.kpool = tail + g.part_o_bytes + g.part_ml_bytes + kClockBytes;
   c->scratch.vpool = (char*)c->scratch.kpool + g.scratch_bytes;
+  hipError_t se = static_scratch_address(&c->static_scratch);  // once per device, cached
+  if (se != hipSuccess) {
+    delete c;
+    return hip_fail(se, "looking up the static scratch");
+  }
   rc = gca_reset(c, stream);
   if (rc != GCA_OK) {
     delete c;
@@ -451,9 +475,10 @@ int gca_anchor_init(gca_ctx* c, int32_t layer, const void* q, const void* k, con
 }
 
 namespace {
-// append: 1 cache frame t, 0 attend only, -1 follow the keyframe schedule
+// append: 1 cache frame t, 0 attend only, -1 follow the keyframe schedule;
+// noalloc: split partials in the static scratch array
 int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
-              float* lse, int append, void* stream) {
+              float* lse, int append, void* stream, bool noalloc = false) {
   int rc = check_ctx_layer(c, layer);
   if (rc != GCA_OK) return rc;
   if (!q || !k || !v || !out) return fail(GCA_E_INVALID_ARG, "q, k, v and out must be non-NULL");
@@ -475,6 +500,15 @@ int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const voi
     return fail(GCA_E_OUT_OF_PAGES, "page pool exhausted at frame " + std::to_string(t));
   if (nsp + new_sum > g.max_sum_pages)  // cannot happen with the list sized for every frame
     return fail(GCA_E_OUT_OF_PAGES, "summary page list full at frame " + std::to_string(t));
+  if (noalloc) {
+    const int npg = n * g.ppf + nsp + w * g.ppf + g.ppf;
+    const int ns = choose_splits(cfg, (int)cdiv(g.F, query_rows(cfg)), npg);
+    const size_t need = partial_bytes(c, g.F, ns, nullptr);
+    if (need > kStaticScratchBytes)
+      return fail(GCA_E_INVALID_ARG, "step " + std::to_string(t) + " needs " + std::to_string(need) +
+                                         " bytes of split partials, more than the " +
+                                         std::to_string(kStaticScratchBytes) + " of the static scratch");
+  }
   hipStream_t st = (hipStream_t)stream;
   // pages of frame t (lowest free first; a non-keyframe gives them back at
   // the end of the step); then, if a keyframe leaves the window, a new
@@ -512,7 +546,7 @@ int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const voi
   pl.f_last_valid = g.f_last_valid;
   const int64_t keys = (int64_t)(n + w + 1) * g.F + (int64_t)S * hs.traj;
   rc = run_step_kernels(c, layer, q, k, v, out, lse, g.F, pl, fresh, key ? slot : -1,
-                        evict ? &ev : nullptr, keys, st);
+                        evict ? &ev : nullptr, keys, st, false, 1, noalloc);
   if (rc != GCA_OK) return rc;
   hs.next = t + 1;
   if (!key) {
@@ -535,6 +569,11 @@ int step_impl(gca_ctx* c, int32_t layer, const void* q, const void* k, const voi
 int gca_step(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v, void* out,
              float* lse, void* stream) {
   return step_impl(c, layer, q, k, v, out, lse, -1, stream);
+}
+
+int gca_step_noalloc(gca_ctx* c, int32_t layer, const void* q, const void* k, const void* v,
+                     void* out, float* lse, void* stream) {
+  return step_impl(c, layer, q, k, v, out, lse, -1, stream, true);
 }
 
 int gca_set_rotary(gca_ctx* c, const float* cos_sin) {

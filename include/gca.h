@@ -122,6 +122,21 @@ int gca_step(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const vo
 int gca_step_keyframe(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
                       void* out, float* lse, int32_t append, void* stream);
 
+/* gca_step for callers that cannot allocate device memory at step time (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same step, with the same kernels and results, except that
+ * the key splits' partial results go to a static device array inside the
+ * library (32 MiB, one per GPU, held until the process ends) instead of the
+ * context's workspace.  The caller still passes the inputs, the outputs and a
+ * context; nothing is allocated and no library allocating routine is called.
+ * Every call on one GPU shares that array, so calls that overlap on one GPU
+ * (other streams, other contexts, other threads) race.  A step whose
+ * partials would need more than the array holds (possible for fp32 frames of
+ * at most 256 rows with many visible pages) returns GCA_E_INVALID_ARG before
+ * anything is enqueued or changed; gca_step serves such a step. */
+int gca_step_noalloc(gca_ctx* ctx, int32_t layer, const void* q, const void* k, const void* v,
+                     void* out, float* lse, void* stream);
+
 /* Rotary position embedding for the calls that follow (technical summary
  * §2.7 and the deep dive's 3D-RoPE switch: the model encodes frame time, and
  * optionally patch position, into Q and K; the frequency schedule is not on
