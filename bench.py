@@ -264,6 +264,10 @@ def main():
         f"{achieved:.1f} TFLOP/s; attention share of wall {attn_avg_ms * timed_launches / 1e3 / elapsed:.2%}; "
         f"shader clock {clock:.2f} GHz")
 
+    phases = phase_summary(prof)
+    if phases:
+        log(f"phase cycles (workgroup 0 of the sampled launches): {json.dumps(phases)}")
+
     variant = [f"keyframe interval {args.keyframe_interval}"] if args.keyframe_interval != 1 else []
     variant += [f"S={S}"] if S != 6 else []
     variant += ["rotary Q/K"] if args.rotary else []
@@ -314,6 +318,8 @@ def main():
             "frac_at_clock": round(achieved / (peak * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
         },
     }
+    if phases:
+        result["phase_cycles"] = phases
     stack.close()
     del pools
     torch.cuda.empty_cache()
@@ -321,6 +327,29 @@ def main():
     if not args.no_cpu_baseline and cfg_no:
         result["cpu_baseline"] = cpu_baseline(args, H, D, M, S, n, k, T, Ly, W, tdt)
     print(json.dumps(result), flush=True)
+
+
+PHASES = ["args_and_split", "page_list", "first_pages", "mfma_phases", "softmax_phases",
+          "barrier_and_copy_waits", "epilogue"]
+
+
+def phase_summary(prof):
+    """Per-launch and per-page phase cycles of a GCA_PHASE_TIMING build (None
+    for the default build, whose phase counters stay zero)."""
+    pc = prof.get("phase_cycles") or []
+    if not any(pc) or prof["attn_launches"] == 0:
+        return None
+    out = {}
+    for g, wave in ((0, "wave0_group_a"), (1, "wave4_group_b")):
+        c = pc[8 * g: 8 * g + 8]
+        pages = c[7]
+        n = prof["attn_launches"]
+        out[wave] = {
+            "per_launch": {name: round(c[i] / n, 1) for i, name in enumerate(PHASES)},
+            "per_page_in_loop": {name: round(c[i] / pages, 1) for i, name in enumerate(PHASES) if 3 <= i <= 5},
+            "pages_per_launch": round(pages / n, 2),
+        }
+    return out
 
 
 def frame_attention_bench(args, cfg, G, torch, dev):

@@ -14,7 +14,10 @@ import os
 import numpy as np
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgca.so")
+# GCA_LIBRARY names another build of the library in the package directory
+# (a compile-time variant of the kernels, see build.py); default libgca.so.
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        os.path.basename(os.environ.get("GCA_LIBRARY", "libgca.so")))
 
 GCA_BF16, GCA_FP32 = 0, 1
 GCA_OK = 0
@@ -61,7 +64,7 @@ class gca_state_host(ctypes.Structure):
 class gca_profile(ctypes.Structure):
     _fields_ = [("attn_ms", ctypes.c_double), ("attn_launches", ctypes.c_int64),
                 ("attn_flop", ctypes.c_double), ("attn_kv_bytes", ctypes.c_double),
-                ("attn_clock_ghz", ctypes.c_double)]
+                ("attn_clock_ghz", ctypes.c_double), ("phase_cycles", ctypes.c_double * 16)]
 
 
 class GcaError(RuntimeError):
@@ -253,7 +256,9 @@ def gca_profile_enable(ctx, on, every: int = 1):
 def gca_profile_read(ctx) -> dict:
     p = gca_profile()
     _check(lib().gca_profile_read(ctx, ctypes.byref(p)))
-    return {name: getattr(p, name) for name, _ in gca_profile._fields_}
+    out = {name: getattr(p, name) for name, _ in gca_profile._fields_}
+    out["phase_cycles"] = list(p.phase_cycles)
+    return out
 
 
 # ---------------------------------------------------------------- convenience

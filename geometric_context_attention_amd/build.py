@@ -23,20 +23,28 @@ def sources():
     return [os.path.join(CSRC, "gca_kernels.hip"), os.path.join(CSRC, "gca_runtime.cpp")]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libgca.so; always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *DEVICE_FLAGS, "-fPIC", "-shared", "-I", os.path.join(ROOT, "include"),
-           *sources(), "-o", tmp]
+def build(verbose: bool = False, defines=(), name: str = "libgca.so") -> str:
+    """Compile every source into libgca.so (or `name`, in the package
+    directory, with extra -D `defines`: the kernels' compile-time variants);
+    always recompiles."""
+    lib = os.path.join(PKG, name)
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *DEVICE_FLAGS, *[f"-D{d}" for d in defines], "-fPIC", "-shared",
+           "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed to build libgca.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra define, e.g. GCA_SOFT_EXP=4")
+    ap.add_argument("--name", default="libgca.so", help="library file name in the package directory")
+    a = ap.parse_args()
+    print(build(verbose=True, defines=a.defines, name=a.name))

@@ -23,6 +23,7 @@
 #include <type_traits>
 #include <vector>
 
+#include "gca_exp2_poly.h"
 #include "gca_internal.h"
 
 namespace gca {
@@ -313,6 +314,63 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #ifndef GCA_AHEAD
 #define GCA_AHEAD 4
 #endif
+// Exponentials of a page computed on the FMA path instead of v_exp_f32: this
+// many of every 16 (0, 4 or 8); see exp2_poly.
+#ifndef GCA_SOFT_EXP
+#define GCA_SOFT_EXP 0
+#endif
+static_assert(GCA_SOFT_EXP == 0 || GCA_SOFT_EXP == 4 || GCA_SOFT_EXP == 8, "a quarter or a half");
+// 1: the older wave group (A, favoured by the issue arbiter) computes its
+// exponent arguments in its softmax phase, the younger one beside its MFMAs.
+#ifndef GCA_ASYM_ARGS
+#define GCA_ASYM_ARGS 0
+#endif
+constexpr bool kAsymArgs = GCA_ASYM_ARGS != 0;
+
+// Phase timing (diagnostic builds, GCA_PHASE_TIMING=1): in workgroup 0 of a
+// sampled launch (AttnArgs::clock set), wave 0 (group A) and wave 4 (group B)
+// add the shader cycles (s_memtime) of each phase of k_attn_bf16 to
+// clock[2 + 8g + i], g = 0 for wave 0 and 1 for wave 4:
+//   i = 0  kernel start to the Q loads issued (arguments, split arithmetic)
+//       1  to the split's page list in LDS
+//       2  to the first pages landed (the loop starts)
+//       3  MFMA phases            4  softmax (VALU) phases
+//       5  waits at the barriers and on the copies
+//       6  the last PV, the epilogue and the output stores
+//       7  pages walked
+// Reading the timer waits on the wave's scalar/LDS counter, so these builds
+// run a little slower; the default build has none of it.
+#ifndef GCA_PHASE_TIMING
+#define GCA_PHASE_TIMING 0
+#endif
+constexpr bool kPhaseTiming = GCA_PHASE_TIMING != 0;
+
+struct PhaseClock {
+  unsigned long long t, acc[8];
+  bool on;
+  __device__ __forceinline__ void start(bool enabled) {
+    on = kPhaseTiming && enabled;
+    if (on) {
+      t = __builtin_amdgcn_s_memtime();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0;
+    }
+  }
+  __device__ __forceinline__ void lap(int i) {
+    if (kPhaseTiming && on) {
+      const unsigned long long n = __builtin_amdgcn_s_memtime();
+      acc[i] += n - t;
+      t = n;
+    }
+  }
+  __device__ __forceinline__ void flush(unsigned long long* clock, int g, int pages, bool lane0) {
+    if (kPhaseTiming && on && lane0) {
+      acc[7] = (unsigned long long)pages;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) atomicAdd(&clock[2 + 8 * g + i], acc[i]);
+    }
+  }
+};
 constexpr int kRing = GCA_RING;    // LDS page slots
 constexpr int kAhead = GCA_AHEAD;  // a wave stages page j + kAhead while it computes page j
 static_assert(kRing >= kAhead + 2, "a slot is refilled only after both wave groups have read it");
@@ -361,6 +419,11 @@ __device__ __forceinline__ void wg_barrier() {
 // register r of tile kt are 32kt + 8(r/4) + 4h + r%4 for lane half h, so the
 // slots form a suffix; a group of four registers is only looked at when the
 // (uniform) key range it covers reaches valid.
+// Score of an empty slot: -inf, or, when some exponentials run on the FMA
+// path, a finite value far below any real score (its exponential is still 0,
+// and the range reduction of exp2_poly stays finite).
+constexpr float kMaskedScore = GCA_SOFT_EXP ? -1e30f : -INFINITY;
+
 template <int NJ>
 __device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf) {
 #pragma unroll
@@ -372,7 +435,7 @@ __device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf
         for (int q = 0; q < 4; ++q) {
           const bool dead = kt * 32 + 8 * g + 4 * hf + q >= valid;
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) sc[kt][j][4 * g + q] = dead ? -INFINITY : sc[kt][j][4 * g + q];
+          for (int j = 0; j < NJ; ++j) sc[kt][j][4 * g + q] = dead ? kMaskedScore : sc[kt][j][4 * g + q];
         }
       }
     }
@@ -383,6 +446,28 @@ __device__ __forceinline__ void mask_page(f32x16 (&sc)[2][NJ], int valid, int hf
 // into x = s * scale * log2 e - m, beside the PV product (see mfma_phase);
 // the VALU phase then only exponentiates.
 //
+// 2^x on the FMA path (Cody-Waite range reduction: 2^x = 2^floor(x) * 2^f
+// with f = x - floor(x) in [0, 1); 2^f from a minimax polynomial by Horner's
+// rule, then an exact ldexp).  The coefficients and the error bound, 7.5e-5
+// relative over the arguments the softmax produces, come from fit_exp2.py.
+// x = -inf is never passed (masked slots are finite when this is used).
+__device__ __forceinline__ float exp2_poly(float x) {
+  const float f = __builtin_amdgcn_fractf(x);
+  const int n = (int)floorf(x);
+  float p = __builtin_fmaf(GCA_EXP2_C3, f, GCA_EXP2_C2);
+  p = __builtin_fmaf(p, f, GCA_EXP2_C1);
+  p = __builtin_fmaf(p, f, GCA_EXP2_C0);
+  return __builtin_amdgcn_ldexpf(p, n);
+}
+static_assert(GCA_EXP2_POLY_DEGREE == 3, "exp2_poly evaluates a cubic");
+
+// Register r of a 16-register score group takes its exponential from
+// exp2_poly when it is one of the GCA_SOFT_EXP of 16 spread evenly.
+__device__ __forceinline__ constexpr bool soft_exp_slot(int r) {
+  return GCA_SOFT_EXP > 0 && r % (16 / (GCA_SOFT_EXP > 0 ? GCA_SOFT_EXP : 16)) ==
+                                 16 / (GCA_SOFT_EXP > 0 ? GCA_SOFT_EXP : 16) - 1;
+}
+
 // p = exp2(x - shift) as packed bf16 P^T fragments (pf[j][kc]: 16-key chunk
 // kc of the page); psum[j] is the sum of the same rounded values over this
 // lane's 32 keys (v_dot2 with (1, 1)).
@@ -395,9 +480,10 @@ __device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        pf[j][kt * 2 + (r >> 3)][r & 7] =
-            (__bf16)__builtin_amdgcn_exp2f(kShift ? sc[kt][j][r] - shift[j] : sc[kt][j][r]);
+      for (int r = 0; r < 16; ++r) {
+        const float x = kShift ? sc[kt][j][r] - shift[j] : sc[kt][j][r];
+        pf[j][kt * 2 + (r >> 3)][r & 7] = (__bf16)(soft_exp_slot(r) ? exp2_poly(x) : __builtin_amdgcn_exp2f(x));
+      }
     float acc = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
@@ -451,9 +537,17 @@ __device__ __forceinline__ void raise_max(const f32x16 (&sc)[2][NJ], float (&m)[
 // values that occurred, P keeps bf16's relative precision.
 constexpr uint32_t kSumLimitBits = 0x47800000u;  // 2^16 as fp32 bits; inf and NaN compare above
 
-template <int NJ>
-__device__ __forceinline__ void valu_phase(const f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
-                                           f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4], bool first) {
+template <int NJ, bool kArgs = false>
+__device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
+                                           f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4], bool first, float c2 = 0.f) {
+  if constexpr (kArgs) {  // the exponent arguments, when the MFMA phase left them
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][j][r] = __builtin_fmaf(sc[kt][j][r], c2, -m[j]);
+  }
   float psum[NJ], shift[NJ];
   page_exp<NJ, false>(sc, shift, pf, psum);
   bool big = first;
@@ -465,6 +559,16 @@ __device__ __forceinline__ void valu_phase(const f32x16 (&sc)[2][NJ], float (&m)
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) l[j] += psum[j];
+}
+
+// Copy rows r0 .. r0+7 of a 64-wide bf16 tile into LDS, swizzled (chunk c of
+// row r at swz(r, c)): lane l takes source chunk (l & 7) ^ ((r >> 1) & 7) of
+// row r0 + (l >> 3) into LDS position 8r + (l & 7); `src_row` gives the
+// row's address (rows past the valid ones repeat a valid one).
+template <class RowPtr>
+__device__ __forceinline__ void copy_rows8(uint16_t* tile, int r0, int lane, RowPtr src_row) {
+  const int r = r0 + (lane >> 3), pc = lane & 7;
+  __builtin_amdgcn_global_load_lds(src_row(r) + ((pc ^ ((r >> 1) & 7)) << 3), tile + r0 * kHeadDim, 16, 0, 0);
 }
 
 // Issue the copy of physical page pg into ring slot `slot` (K and V tiles):
@@ -488,7 +592,7 @@ __device__ __forceinline__ void stage_page(const AttnArgs& a, uint16_t (&ring)[2
 // from slot sv) with, beside it, the scores turned in place into
 // x = s * c2 - m (c2 = scale * log2 e): the VALU works while the matrix core
 // does, and its work fills the waits on the V operand reads.
-template <int NJ>
+template <int NJ, bool kArgs = true>
 __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* sv, const bf16x8 (&qf)[NJ][4],
                                            const bf16x8 (&pf)[NJ][4], f32x16 (&o)[2][NJ], f32x16 (&sc)[2][NJ],
                                            const float (&m)[NJ], float c2, int valid, int l32, int hf) {
@@ -523,7 +627,7 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       o[i % 2][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j][i / 2], o[i % 2][j], 0, 0, 0);
-      if (sk != nullptr) {
+      if (kArgs && sk != nullptr) {
         // multiply-adds 4u .. 4u+3 of the 64 (u = 2i + j): tile (u / 8, u / 4 % 2), registers 4(u % 4) ..
         const int u = 2 * i + j;
         const int kt = (u >> 3) & 1, jq = (u >> 2) & 1, r0 = (u & 3) * 4;
@@ -533,7 +637,7 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (sk != nullptr) {
+  if (kArgs && sk != nullptr) {
     // keep the multiply-adds here: without a use the compiler would sink them
     // into the VALU phase
 #pragma unroll
@@ -748,6 +852,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hf = lane >> 5, l32 = lane & 31;
+  PhaseClock pc;
+  pc.start(a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && (wave == 0 || wave == 4));
   int h, qb, s;
   decode_wg(a, h, qb, s);
   const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
@@ -766,6 +872,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
 
   bf16x8 qf[NJ][4];
   load_q<NJ>(a, qf, h, qb, wave, l32, hf);
+  pc.lap(0);
 
   const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
   const int np = p1 - p0;                // >= 1: there are never more splits than pages
@@ -777,6 +884,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     plist[i - p0] = page_entry(a, raw, valid);
   }
   __syncthreads();
+  pc.lap(1);
   // list entry (page id << 7 | valid slots) of split page i, clamped to the
   // last one (the ring is kept full past the end with copies of that page)
   auto entry = [&](int i) { return __builtin_amdgcn_readfirstlane(plist[(i < np ? i : np - 1)]); };
@@ -828,6 +936,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   GCA_WAIT_VMCNT(2 * (kAhead - 2));
   wg_barrier();
   if (!grp_a) wg_barrier();  // group B runs one phase behind
+  pc.lap(2);
 
   f32x16 sc[2][NJ];
   // the MFMA phase of the first page multiplies this zero P with the V tile
@@ -839,23 +948,37 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
-  auto page_step = [&](int jj, auto slot_c) {
-    constexpr int S = decltype(slot_c)::value;  // ring slot of page p0 + jj
-    constexpr int SA = (S + kAhead) % kRing;    // slot page p0 + jj + kAhead goes to
-    // the entry after that one is read before the MFMA phase's own LDS reads,
-    // so it has landed by the time it is used
-    const uint32_t raw_next = plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
-    mfma_phase<NJ>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2, (int)(ent[S] & 127u),
-                   l32, hf);
-    if (GCA_PINGPONG) wg_barrier();
-    ent[SA] = ent_ahead;
-    stage_page(a, ring, SA, (int)(ent_ahead >> 7), h, tid);
-    ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
-    valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
-    GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
-    wg_barrier();
+  // the page loop; kA: this wave computes its exponent arguments in its
+  // softmax phase (group A of the asymmetric variant), else beside its MFMAs.
+  // The two kinds of wave run separate copies of the loop.
+  auto run_pages = [&](auto asym_c) {
+    constexpr bool kA = decltype(asym_c)::value;
+    auto page_step = [&](int jj, auto slot_c) {
+      constexpr int S = decltype(slot_c)::value;  // ring slot of page p0 + jj
+      constexpr int SA = (S + kAhead) % kRing;    // slot page p0 + jj + kAhead goes to
+      // the entry after that one is read before the MFMA phase's own LDS reads,
+      // so it has landed by the time it is used
+      const uint32_t raw_next = plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
+      mfma_phase<NJ, !kA>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                          (int)(ent[S] & 127u), l32, hf);
+      pc.lap(3);
+      if (GCA_PINGPONG) wg_barrier();
+      pc.lap(5);
+      ent[SA] = ent_ahead;
+      stage_page(a, ring, SA, (int)(ent_ahead >> 7), h, tid);
+      ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
+      valu_phase<NJ, kA>(sc, m, l, o, pf, jj == 0, c2);
+      pc.lap(4);
+      GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
+      wg_barrier();
+      pc.lap(5);
+    };
+    for (int jj = 0; jj < np; jj += kRing) for_each_slot<0, kRing>(jj, np, page_step);
   };
-  for (int jj = 0; jj < np; jj += kRing) for_each_slot<0, kRing>(jj, np, page_step);
+  if (kAsymArgs && grp_a)
+    run_pages(std::true_type{});
+  else
+    run_pages(std::false_type{});
   // PV of the last page; group A then takes the barrier that group B took
   // first, so both have passed the same number
   mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], qf, pf, o, sc, m, c2, kPage, l32, hf);
@@ -867,6 +990,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
+  }
+  if constexpr (kPhaseTiming) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the output stores have completed
+    pc.lap(6);
+    pc.flush(a.clock, wave >= 4, np, lane == 0);
   }
 }
 
@@ -1012,15 +1140,6 @@ constexpr int kWsTilesBytes = (kWsQElems + 2 * kAttnWaves * kTileElems) * 2;
 constexpr int kWsExBytes = kAttnWaves * kWsRows * kWsPad * 4;
 static_assert(kWsExBytes <= kWsTilesBytes, "the O exchange fits in the tiles' space");
 
-// Copy rows r0 .. r0+7 of a 64-wide bf16 tile into LDS, swizzled (chunk c of
-// row r at swz(r, c)): lane l takes source chunk (l & 7) ^ ((r >> 1) & 7) of
-// row r0 + (l >> 3) into LDS position 8r + (l & 7); `src_row` gives the
-// row's address (rows past the valid ones repeat a valid one).
-template <class RowPtr>
-__device__ __forceinline__ void copy_rows8(uint16_t* tile, int r0, int lane, RowPtr src_row) {
-  const int r = r0 + (lane >> 3), pc = lane & 7;
-  __builtin_amdgcn_global_load_lds(src_row(r) + ((pc ^ ((r >> 1) & 7)) << 3), tile + r0 * kHeadDim, 16, 0, 0);
-}
 
 __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs a_in) {
   const AttnArgs a = batch_frame<2>(a_in);

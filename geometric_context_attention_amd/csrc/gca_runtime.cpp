@@ -34,6 +34,7 @@ int hip_fail(hipError_t e, const char* what) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr size_t kClockBytes = 256;  // profiling counters at the end of the workspace
+constexpr int kClockSlots = 18;      // shader cycles, reference ticks, 16 phase counters
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Derived sizes and workspace layout of a configuration.
@@ -239,7 +240,7 @@ struct gca_ctx {
   unsigned long long* clock = nullptr;  // [2] device: shader cycles, reference ticks
   LayerDev scratch{};                   // ppf K/V pages for frame attention (pools only)
   const float2* rope = nullptr;         // rotary table of the next calls (gca_set_rotary)
-  unsigned long long clock_base[2] = {0, 0};
+  unsigned long long clock_base[kClockSlots] = {};
   bool f32 = false;
   // profiling
   bool prof = false;
@@ -778,11 +779,12 @@ int gca_profile_read(gca_ctx* c, gca_profile* out) {
   out->attn_flop = c->attn_flop;
   out->attn_kv_bytes = c->attn_bytes;
   out->attn_clock_ghz = 0.0;
-  unsigned long long now[2];
+  unsigned long long now[kClockSlots];
   hipError_t r = hipMemcpy(now, c->clock, sizeof(now), hipMemcpyDeviceToHost);
   if (r != hipSuccess) return hip_fail(r, "reading the clock counters");
   const unsigned long long cyc = now[0] - c->clock_base[0], ticks = now[1] - c->clock_base[1];
   if (ticks > 0) out->attn_clock_ghz = 0.1 * (double)cyc / (double)ticks;
+  for (int i = 0; i < 16; ++i) out->phase_cycles[i] = (double)(now[2 + i] - c->clock_base[2 + i]);
   return GCA_OK;
 }
 

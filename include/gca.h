@@ -257,6 +257,12 @@ typedef struct {
   double attn_clock_ghz; /* shader clock during the bf16 attention launches, from
                             the cycle and 100 MHz reference counters that one
                             workgroup per launch samples; 0 if none ran */
+  double phase_cycles[16]; /* builds with GCA_PHASE_TIMING=1 only (else 0): summed
+                              shader cycles of the bf16 attention's phases in
+                              workgroup 0 of the sampled launches, waves 0 and 4
+                              ([8g + i]: i = 0 arguments and split arithmetic, 1 page
+                              list, 2 first pages, 3 MFMA phases, 4 softmax phases,
+                              5 barrier and copy waits, 6 epilogue, 7 pages) */
 } gca_profile;
 
 /* HIP-event timing of the context's attention launches: on = N > 0 times

@@ -298,3 +298,100 @@ def test_corrupted_tables_are_flagged():
     st.reset()
     assert st.export_state(0)["device_error"] == 0
     st.close()
+
+
+def _swap23(s):
+    return (s & ~12) | ((s & 4) << 1) | ((s & 8) >> 1)
+
+
+def test_poisoned_padding_slots_change_nothing():
+    """The empty slots of partial pages (a frame's last page, the summary tail
+    page) are masked: filled with huge finite values before every step, they
+    leave every output bit unchanged (their scores are masked before the max,
+    and their probability is exactly 0)."""
+    H, M, n, k, T = 4, 100, 3, 4, 24
+    F = M + 6
+    cfg = G.make_config(num_heads=H, image_tokens=M, n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_BF16)
+    clean, dirty = G.GcaStack(cfg), G.GcaStack(cfg)
+    spec = StreamSpec(H=H, D=64, M=M, dtype=torch.bfloat16, seed=9, chunk=16)
+    q, kx, v = (t.cuda() for t in draw_frames(spec, 0, 0, T))
+    rows = n * F
+    poison = torch.tensor(1e30, dtype=torch.bfloat16)
+    ppf, last_valid = 2, F - 64
+
+    def poison_padding(st):
+        kp, vp = st.pools(0)
+        s = st.export_state(0)
+        pages = [int(p) for p in s["frame_table"][:, ppf - 1] if p >= 0]
+        spans = [(p, last_valid) for p in pages]
+        ns = s["n_summary_pages"]
+        if ns:
+            tail_valid = 6 * s["n_traj"] - 64 * (ns - 1)
+            spans.append((int(s["summary_pages"][ns - 1]), tail_valid))
+        for p, valid in spans:
+            if valid >= 64:
+                continue
+            kp[p, :, valid:, :] = poison
+            cols = torch.as_tensor(_swap23(np.arange(valid, 64)), device="cuda")
+            vp[p, :, :, cols] = poison
+        torch.cuda.synchronize()
+
+    outs = []
+    for st in (clean, dirty):
+        st.anchor_init(0, q[:n].reshape(rows, H, 64), kx[:n].reshape(rows, H, 64), v[:n].reshape(rows, H, 64))
+    for t in range(n, T):
+        poison_padding(dirty)
+        oc, lc = clean.step(0, q[t], kx[t], v[t])
+        od, ld = dirty.step(0, q[t], kx[t], v[t])
+        assert torch.equal(oc.view(torch.int16), od.view(torch.int16)), f"step {t}: outputs differ"
+        assert torch.equal(lc, ld), f"step {t}: LSE differs"
+        outs.append(t)
+    assert dirty.export_state(0)["device_error"] == 0
+    clean.close()
+    dirty.close()
+
+
+def test_page_order_does_not_change_the_result():
+    """Attention over a page list does not depend on the order of its pages:
+    two window frames' page-table entries swapped on the device (the same keys,
+    walked in another order and cut into other splits) give the output of the
+    unshuffled twin to fp32 rounding; swapped back, the stream goes on with
+    consistent state."""
+    H, M, n, k, T = 2, 100, 3, 6, 16
+    F = M + 6
+    cfg = G.make_config(num_heads=H, image_tokens=M, n_anchor=n, k_window=k, max_frames=T, dtype=G.GCA_FP32)
+    a, b = G.GcaStack(cfg), G.GcaStack(cfg)
+    spec = StreamSpec(H=H, D=64, M=M, dtype=torch.float32, seed=10, chunk=16)
+    q, kx, v = (t.cuda() for t in draw_frames(spec, 0, 0, T))
+    rows = n * F
+    for st in (a, b):
+        st.anchor_init(0, q[:n].reshape(rows, H, 64), kx[:n].reshape(rows, H, 64), v[:n].reshape(rows, H, 64))
+    swapped_steps = 0
+    for t in range(n, T):
+        s = b.export_state(0)
+        ft = s["frame_table"]
+        ppf = s["pages_per_frame"]
+        # two cached frames in the middle of the window (neither leaves the cache at this step),
+        # plus anchor frames 0 and 2
+        pairs = [(0, 2)]
+        if t - n >= 4:
+            pairs.append((t - 3, t - 2))
+        for f1, f2 in pairs:
+            for j in range(ppf):
+                G.gca_debug_set_table_entry(b.ctx, 0, 0, f1 * ppf + j, int(ft[f2, j]))
+                G.gca_debug_set_table_entry(b.ctx, 0, 0, f2 * ppf + j, int(ft[f1, j]))
+        assert b.export_state(0)["device_error"] == G.GCA_ERR_TABLE_MISMATCH
+        oa, la = a.step(0, q[t], kx[t], v[t])
+        ob, lb = b.step(0, q[t], kx[t], v[t])
+        err = float((oa - ob).abs().max())
+        assert err <= 2e-6, f"step {t}: shuffled pages change the output by {err}"
+        assert float((la - lb).abs().max()) <= 2e-6
+        for f1, f2 in pairs:  # restore the true entries
+            for j in range(ppf):
+                G.gca_debug_set_table_entry(b.ctx, 0, 0, f1 * ppf + j, int(ft[f1, j]))
+                G.gca_debug_set_table_entry(b.ctx, 0, 0, f2 * ppf + j, int(ft[f2, j]))
+        assert b.export_state(0)["device_error"] == 0
+        swapped_steps += 1
+    assert swapped_steps == T - n
+    a.close()
+    b.close()
