@@ -1315,107 +1315,275 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
   }
 }
 
-// fp32 attention: one thread per query row (256-row blocks).  Each page is
-// staged in LDS; keys are taken one at a time with an online softmax.
-__global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a_in) {
+// fp32 attention on the matrix cores (v_mfma_f32_32x32x2_f32): one workgroup
+// = (head, 256 query rows, one key split), 4 waves; wave w owns query rows
+// [64w, 64w+64) of the block as two 32-row tiles j.  Per 64-slot page:
+//   S^T[key][q] = K Q^T   A = K (LDS), B = Q^T (registers); step i of the 32
+//                         contracts d = i in lane half 0 and d = 32 + i in
+//                         lane half 1
+//   exact online softmax per query column: the page's row max, then
+//                         p = exp2((s - m) * scale * log2 e) in fp32
+//   O^T[d][q] += V^T P^T  A = V^T (LDS), B = P^T: step r of a 32-key tile
+//                         contracts the two keys register r of the S^T
+//                         accumulator holds in the two lane halves (keys
+//                         8(r/4) + 4h + r%4), so P^T comes straight from that
+//                         register; the V^T columns are in the pool's swap23
+//                         order, which puts a lane's four keys of register
+//                         group r/4 in one 16-byte chunk
+// Operand layout of the 32x32x2 MFMA: A lane l holds row l%32, k = l/32; B
+// lane l holds column l%32, same k; accumulator as in k_attn_bf16.
+// Tiles are fp32 [64][64] with 16-byte chunk c of row r at chunk c ^ (r & 15),
+// so reads of one chunk column by 16 lanes of different rows hit 16 different
+// bank groups.  Two page slots: page j+1 is copied into LDS with
+// global_load_lds while page j is computed.  Pages of the appended frame are
+// built from the input rows instead (keys rotated when rotary angles are
+// given, values transposed) and written to their pool pages by the
+// workgroups of query block 0.
+constexpr int kF32Waves = kF32Rows / 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// float index of 16-byte chunk c of row r in a swizzled fp32 64x64 tile
+__device__ __forceinline__ int swz32(int r, int c) { return r * 64 + ((c ^ (r & 15)) << 2); }
+
+// Copy one fp32 64x64 tile (16 KB) from memory into a swizzled LDS tile:
+// instruction u of wave w moves rows 4(4w + u) .. +3, lane l fetching the
+// source chunk that belongs at LDS chunk position l & 15 of row l >> 4.
+__device__ __forceinline__ void copy_tile_f32(const float* src, float* tile, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r0 = (wave * 4 + u) * 4;
+    const int r = r0 + (lane >> 4), pc = lane & 15;
+    __builtin_amdgcn_global_load_lds(src + r * 64 + ((pc ^ (r & 15)) << 2), tile + r0 * 64, 16, 0, 0);
+  }
+}
+
+// Tiles of page fj of the appended frame from the input rows (all 256
+// threads): K rows (rotated when rotary angles are given), V transposed into
+// columns swap23(slot); slots past `valid` are zero.
+__device__ __forceinline__ void build_fresh_f32(const AttnArgs& a, float* kt, float* vt, int fj, int valid, int h,
+                                                int tid) {
+  constexpr int D = kHeadDim;
+  const float* kin = reinterpret_cast<const float*>(a.k_in);
+  const float* vin = reinterpret_cast<const float*>(a.v_in);
+  for (int e = tid; e < kPage * D / 4; e += kF32Rows) {
+    const int r = e >> 4, c = e & 15;  // slot r, channels 4c .. 4c+3
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+    if (r < valid) {
+      const size_t row = (size_t)fj * kPage + r;
+      const size_t src = (row * a.H + h) * D + 4 * c;
+      kv = *reinterpret_cast<const float4*>(kin + src);
+      vv = *reinterpret_cast<const float4*>(vin + src);
+      if (a.rope != nullptr) {
+        rope_rotate(kv.x, kv.y, a.rope[row * (D / 2) + 2 * c]);
+        rope_rotate(kv.z, kv.w, a.rope[row * (D / 2) + 2 * c + 1]);
+      }
+    }
+    *reinterpret_cast<float4*>(&kt[swz32(r, c)]) = kv;
+    const int col = swap23(r);
+    vt[swz32(4 * c + 0, col >> 2) + (col & 3)] = vv.x;
+    vt[swz32(4 * c + 1, col >> 2) + (col & 3)] = vv.y;
+    vt[swz32(4 * c + 2, col >> 2) + (col & 3)] = vv.z;
+    vt[swz32(4 * c + 3, col >> 2) + (col & 3)] = vv.w;
+  }
+}
+
+// The built tiles of an appended-frame page into its pool page (the caller
+// has synchronised the workgroup after building them).
+__device__ __forceinline__ void store_fresh_f32(const AttnArgs& a, const float* kt, const float* vt, int pg, int h,
+                                                int tid) {
+  const size_t off = ((size_t)pg * a.H + h) * (kPage * kHeadDim);
+  float* kpool = reinterpret_cast<float*>(a.kpool) + off;
+  float* vpool = reinterpret_cast<float*>(a.vpool) + off;
+  for (int e = tid; e < kPage * kHeadDim / 4; e += kF32Rows) {
+    const int r = e >> 4, c = e & 15;
+    *reinterpret_cast<float4*>(kpool + r * 64 + 4 * c) = *reinterpret_cast<const float4*>(&kt[swz32(r, c)]);
+    *reinterpret_cast<float4*>(vpool + r * 64 + 4 * c) = *reinterpret_cast<const float4*>(&vt[swz32(r, c)]);
+  }
+}
+
+__global__ __launch_bounds__(kF32Rows) void k_attn_f32(AttnArgs a_in) {
   const AttnArgs a = batch_frame<4>(a_in);
-  constexpr int D = kHeadDim, P = kPage;
-  __shared__ float sK[P][D + 1];
-  __shared__ float sV[D][P + 1];
+  constexpr int D = kHeadDim, NJ = 2;
+  // two page slots, each a K tile and a V^T tile
+  __shared__ __attribute__((aligned(16))) float lds[2][2][64 * 64];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hf = lane >> 5, l32 = lane & 31;
   int h, qb, s;
   decode_wg(a, h, qb, s);
   const int H = a.H;
-  const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
   const int p0 = split_begin(a, s);
   const int p1 = split_begin(a, s + 1);
+  const int np = p1 - p0;  // >= 1
   if (a.pl.fresh_cnt > 0 && a.fresh_frame >= 0 && blockIdx.x == 0) record_fresh_frame(a);
-  const int row = qb * kF32Rows + threadIdx.x;
-  const bool live = row < a.Lq;
-  const float* q = reinterpret_cast<const float*>(a.q);
-  float qv[D], o[D];
+
+  // Q^T fragments: qf[j][i] = Q[row 32j + l32 of the wave][32hf + i]
+  float qf[NJ][32];
+  const float* qin = reinterpret_cast<const float*>(a.q);
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qv[d] = live ? q[((size_t)row * H + h) * D + d] : 0.f;
-    o[d] = 0.f;
-  }
-  if (live && a.rope != nullptr) {
+  for (int j = 0; j < NJ; ++j) {
+    const int row = qb * kF32Rows + wave * 64 + j * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < D / 2; ++i) rope_rotate(qv[2 * i], qv[2 * i + 1], a.rope[(size_t)row * (D / 2) + i]);
+    for (int u = 0; u < 8; ++u) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row < a.Lq) {
+        v = *reinterpret_cast<const float4*>(qin + ((size_t)row * H + h) * D + 32 * hf + 4 * u);
+        if (a.rope != nullptr) {
+          const float2* cs = a.rope + (size_t)row * (D / 2) + 16 * hf + 2 * u;
+          rope_rotate(v.x, v.y, cs[0]);
+          rope_rotate(v.z, v.w, cs[1]);
+        }
+      }
+      qf[j][4 * u + 0] = v.x;
+      qf[j][4 * u + 1] = v.y;
+      qf[j][4 * u + 2] = v.z;
+      qf[j][4 * u + 3] = v.w;
+    }
   }
-  float m = -INFINITY, l = 0.f;
+
+  f32x16 o[2][NJ];
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
+  float m[NJ], l[NJ];  // running row max (raw score units) and this lane's share of the row sum
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+  }
   const float c2 = a.scale_log2;
-  float* kpool = reinterpret_cast<float*>(a.kpool);
-  float* vpool = reinterpret_cast<float*>(a.vpool);
-  const float* kin = reinterpret_cast<const float*>(a.k_in);
-  const float* vin = reinterpret_cast<const float*>(a.v_in);
-  for (int i = p0; i < p1; ++i) {
+  const float* kpool = reinterpret_cast<const float*>(a.kpool);
+  const float* vpool = reinterpret_cast<const float*>(a.vpool);
+
+  // page i of the split into slot sl: a cached page by DMA (returns true),
+  // an appended-frame page not (it is built when its turn comes)
+  auto stage = [&](int i, int sl) {
     int valid, fj;
-    const int pg = map_page(a, i, valid, fj);
-    const size_t off = ((size_t)pg * H + h) * (P * D);
+    const int pg = map_page(a, p0 + i, valid, fj);
+    if (fj >= 0) return false;
+    const size_t off = ((size_t)pg * H + h) * (kPage * D);
+    copy_tile_f32(kpool + off, lds[sl][0], wave, lane);
+    copy_tile_f32(vpool + off, lds[sl][1], wave, lane);
+    return true;
+  };
+  bool staged = stage(0, 0);
+  for (int jj = 0; jj < np; ++jj) {
+    const int sl = jj & 1;
+    const bool next = jj + 1 < np && stage(jj + 1, sl ^ 1);
+    // this wave's copies of page jj have landed (8 copies of page jj+1 may be in flight)
+    if (next)
+      GCA_WAIT_VMCNT(8);
+    else
+      GCA_WAIT_VMCNT(0);
     __syncthreads();
-    if (fj < 0) {
-      for (int e = threadIdx.x; e < P * D; e += 256) {
-        sK[e / D][e % D] = kpool[off + e];
-        sV[e / P][e % P] = vpool[off + e];
+    int valid, fj;
+    const int pg = map_page(a, p0 + jj, valid, fj);
+    float* kt = lds[sl][0];
+    float* vt = lds[sl][1];
+    if (!staged && fj >= 0) {  // uniform: the appended frame's page, built here
+      build_fresh_f32(a, kt, vt, fj, valid, h, tid);
+      __syncthreads();
+      if (qb == 0) store_fresh_f32(a, kt, vt, pg, h, tid);
+    }
+    staged = next;
+
+    // S^T = K Q^T
+    f32x16 sc[2][NJ];
+#pragma unroll
+    for (int kt_i = 0; kt_i < 2; ++kt_i) {
+      const int row = kt_i * 32 + l32;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt_i][j][r] = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const f32x4 kf = *reinterpret_cast<const f32x4*>(&kt[swz32(row, 8 * hf + u)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            sc[kt_i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[j][4 * u + e], sc[kt_i][j], 0, 0, 0);
       }
-    } else {
-      for (int e = threadIdx.x; e < P * D; e += 256) {
-        const int r = e / D, d = e % D;
-        float kv = 0.f, vv = 0.f;
-        if (r < valid) {
-          const size_t src = ((size_t)(fj * P + r) * H + h) * D + d;
-          kv = kin[src];
-          vv = vin[src];
+    }
+    if (valid < kPage) mask_page<NJ>(sc, valid, hf);
+    // online softmax: the page's row max raises m, l and O are rescaled
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt_i = 0; kt_i < 2; ++kt_i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kt_i][j][r]);
+      const float m_new = fmaxf(m[j], half_pair_max(mx));  // finite: every page holds a visible key
+      const float alpha = exp2f((m[j] - m_new) * c2);    // 0 on the split's first page
+      const float mc = m_new * c2;
+      float ps = 0.f;
+#pragma unroll
+      for (int kt_i = 0; kt_i < 2; ++kt_i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt_i][j][r], c2, -mc));
+          sc[kt_i][j][r] = p;
+          ps += p;
         }
-        sK[r][d] = kv;
-        sV[d][swap23(r)] = vv;
-      }
-      if (a.rope != nullptr) {  // rotated keys are what the cache holds
-        __syncthreads();
-        for (int e = threadIdx.x; e < P * D / 2; e += 256) {
-          const int r = e / (D / 2), i = e % (D / 2);
-          if (r < valid) rope_rotate(sK[r][2 * i], sK[r][2 * i + 1], a.rope[(size_t)(fj * P + r) * (D / 2) + i]);
+      l[j] = l[j] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][j][r] *= alpha;
+      m[j] = m_new;
+    }
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const int drow = dt * 32 + l32;
+#pragma unroll
+      for (int kt_i = 0; kt_i < 2; ++kt_i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          // keys 32kt + 8g + 4hf + q (q = 0..3) sit at columns 32kt + 16(g>>1) + 8hf + 4(g&1) + q
+          const f32x4 vf = *reinterpret_cast<const f32x4*>(
+              &vt[swz32(drow, 8 * kt_i + 4 * (g >> 1) + 2 * hf + (g & 1))]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+              o[dt][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf[q], sc[kt_i][j][4 * g + q], o[dt][j], 0, 0, 0);
         }
-      }
     }
-    __syncthreads();
-    if (fj >= 0 && qb == 0) {
-      for (int e = threadIdx.x; e < P * D; e += 256) {
-        kpool[off + e] = sK[e / D][e % D];
-        vpool[off + e] = sV[e / P][e % P];
-      }
-    }
-#pragma unroll 1
-    for (int key = 0; key < valid; ++key) {
-      float acc = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qv[d], sK[key][d], acc);
-      if (acc > m) {
-        const float alpha = exp2f((m - acc) * c2);
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= alpha;
-        m = acc;
-      }
-      const float p = exp2f((acc - m) * c2);
-      l += p;
-      const int col = swap23(key);
-#pragma unroll
-      for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(p, sV[d][col], o[d]);
-    }
+    __syncthreads();  // every wave is done with slot sl: page jj+2 may go there
   }
-  if (!live) return;
-  if (a.nsplit == 1) {
-    const float inv = 1.f / l;
-    float* out = reinterpret_cast<float*>(a.out) + ((size_t)row * H + h) * D;
+
+  // outputs: register r of o[dt][j] holds d = 32dt + 8(r/4) + 4hf + r%4 of row 32j + l32
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[d] = o[d] * inv;
-    if (a.lse != nullptr) a.lse[(size_t)h * a.Lq + row] = m * a.scale + logf(l);
-  } else {
-    float* po = reinterpret_cast<float*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+  for (int j = 0; j < NJ; ++j) {
+    const float lt = half_pair_sum(l[j]);
+    const int row = qb * kF32Rows + wave * 64 + j * 32 + l32;
+    if (row >= a.Lq) continue;
+    if (a.nsplit == 1) {
+      const float inv = 1.f / lt;
+      float* out = reinterpret_cast<float*>(a.out) + ((size_t)row * H + h) * D;
 #pragma unroll
-    for (int d = 0; d < D; ++d) po[d] = o[d];
-    a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m, l);
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(out + 32 * dt + 8 * g + 4 * hf) =
+              make_float4(o[dt][j][4 * g] * inv, o[dt][j][4 * g + 1] * inv, o[dt][j][4 * g + 2] * inv,
+                          o[dt][j][4 * g + 3] * inv);
+      if (a.lse != nullptr && hf == 0) a.lse[(size_t)h * a.Lq + row] = m[j] * a.scale + logf(lt);
+    } else {
+      float* po = reinterpret_cast<float*>(a.part_o) + (((size_t)h * a.nsplit + s) * a.Lq_pad + row) * D;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(po + 32 * dt + 8 * g + 4 * hf) =
+              make_float4(o[dt][j][4 * g], o[dt][j][4 * g + 1], o[dt][j][4 * g + 2], o[dt][j][4 * g + 3]);
+      if (hf == 0) a.part_ml[((size_t)h * a.nsplit + s) * a.Lq_pad + row] = make_float2(m[j], lt);
+    }
   }
 }
 

@@ -56,6 +56,61 @@ def summarize_pmc(path: str, kernel: str) -> dict:
             for k in sorted(acc)}
 
 
+def trace_report(stats_csv: str, title: str, workload: str, commands, bench_line: str | None = None) -> str:
+    """Text summary of a ``rocprofv3 --kernel-trace --stats`` run for
+    ``profiles/``: what was run, the kernel source digest, the per-kernel
+    table and, if given, the bench JSON line the traced run printed."""
+    out = [f"# {title}", "#", f"# Workload: {workload}", "#",
+           "# Commands (from the repository root, TMPDIR=/tmp):"]
+    out += [f"#   {c}" for c in commands]
+    out += ["#", f"# kernel_source_sha256: {kernel_source_digest()}", "", summarize_kernel_stats(stats_csv)]
+    if bench_line:
+        out += ["", "# Bench line printed by the traced run:", "#   " + bench_line.strip()]
+    return "\n".join(out) + "\n"
+
+
+def pmc_per_dispatch(path: str, kernel: str, counter: str) -> float:
+    """Mean per-dispatch value of one counter for the kernels whose name
+    contains `kernel` in a ``rocprofv3 --pmc`` CSV."""
+    v = summarize_pmc(path, kernel).get(counter)
+    if v is None:
+        raise KeyError(f"{counter} not found for {kernel} in {path}")
+    return v["per_dispatch"]
+
+
+def counter_total(path: str, kernel: str, counter: str) -> float:
+    v = summarize_pmc(path, kernel).get(counter)
+    return 0.0 if v is None else v["total"]
+
+
+def traffic_report(fetch_csv: str, write_csv: str, cal_fetch_csv: str, cal_write_csv: str, kernel: str,
+                   kv_bytes: float, cal_read: float, cal_written: float, workload: str, commands) -> str:
+    """Calibrated HBM bytes per dispatch of `kernel` from two ``--pmc`` runs
+    (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
+    counter reads for the copy calibration (``bench.py --copy-calibration``:
+    `cal_read` bytes read and `cal_written` written by its elementwise
+    kernels).  The result is the traffic file bench.py reads."""
+    f = pmc_per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
+    w = pmc_per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    cf = counter_total(cal_fetch_csv, "elementwise", "FETCH_SIZE")
+    cw = counter_total(cal_write_csv, "elementwise", "WRITE_SIZE")
+    sf = cal_read / (cf * 1024.0)
+    sw = cal_written / (cw * 1024.0)
+    fb, wb = f * 1024.0 * sf, w * 1024.0 * sw
+    out = [f"# {kernel} HBM traffic per launch (rocprofv3 counters)", "#", f"# Workload: {workload}", "#",
+           "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:"]
+    out += [f"#   {c}" for c in commands]
+    out += ["#",
+            f"# Raw (KiB per dispatch): FETCH_SIZE {f:.1f}, WRITE_SIZE {w:.1f}",
+            f"# Calibration (elementwise copy kernels): FETCH_SIZE {cf:.6g} KiB for {cal_read:.6g} B read,",
+            f"#   WRITE_SIZE {cw:.6g} KiB for {cal_written:.6g} B written => scale x{sf:.4f} / x{sw:.4f}",
+            f"# Algorithmic K/V bytes per launch: {kv_bytes:.6g}; calibrated fetch is {fb / kv_bytes:.3f}x that",
+            "", f"kernel_source_sha256: {kernel_source_digest()}",
+            f"fetch_bytes_per_launch: {fb:.6g}", f"write_bytes_per_launch: {wb:.6g}",
+            f"hbm_bytes_per_launch: {fb + wb:.6g}"]
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str = TRAFFIC_FILE):
     """Calibrated HBM bytes per attention launch from the stored counter
     summary, or None if absent or taken on a different kernel source."""
@@ -83,7 +138,37 @@ def main(argv=None):
     b.add_argument("csv")
     b.add_argument("kernel")
     sub.add_parser("digest")
+    t = sub.add_parser("trace-report")
+    t.add_argument("csv")
+    t.add_argument("--title", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--command", action="append", default=[])
+    t.add_argument("--bench-json", help="file whose last line is the bench JSON line of the traced run")
+    t.add_argument("--out", required=True)
+    r = sub.add_parser("traffic-report")
+    for name in ("fetch", "write", "cal_fetch", "cal_write"):
+        r.add_argument("--" + name.replace("_", "-"), required=True)
+    r.add_argument("--kernel", default="k_attn_bf16")
+    r.add_argument("--kv-bytes", type=float, required=True, help="algorithmic K/V bytes per launch")
+    r.add_argument("--cal-read", type=float, required=True)
+    r.add_argument("--cal-written", type=float, required=True)
+    r.add_argument("--workload", required=True)
+    r.add_argument("--command", action="append", default=[])
+    r.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+    if args.cmd == "traffic-report":
+        with open(args.out, "w") as fh:
+            fh.write(traffic_report(args.fetch, args.write, args.cal_fetch, args.cal_write, args.kernel,
+                                    args.kv_bytes, args.cal_read, args.cal_written, args.workload, args.command))
+        return 0
+    if args.cmd == "trace-report":
+        line = None
+        if args.bench_json and os.path.exists(args.bench_json):
+            lines = [x for x in open(args.bench_json).read().splitlines() if x.strip().startswith("{")]
+            line = lines[-1] if lines else None
+        with open(args.out, "w") as fh:
+            fh.write(trace_report(args.csv, args.title, args.workload, args.command, line))
+        return 0
     if args.cmd == "stats":
         print(summarize_kernel_stats(args.csv))
     elif args.cmd == "pmc":
