@@ -75,6 +75,12 @@ def test_tiny_fp32_stream_full_state():
     _run_stream("fp32", M=32, n=3, k=4, T=64, H=2)
 
 
+def test_fp32_paper_frame_shape():
+    """fp32 on the matrix cores at M = 500 + 6: two 256-row query blocks per
+    step, six in the anchor block, a ragged last page (58 rows), 16 heads."""
+    _run_stream("fp32", M=500, n=3, k=4, T=14, H=16, state_every=3)
+
+
 def test_tiny_fp32_single_split():
     _run_stream("fp32", M=32, n=3, k=4, T=40, H=2, max_splits=1, state_every=8)
 

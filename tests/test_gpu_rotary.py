@@ -23,7 +23,8 @@ pytestmark = pytest.mark.gpu
 DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 
-@pytest.mark.parametrize("mode,M,H,k,T", [("fp32", 32, 2, 4, 30), ("bf16", 181, 4, 3, 24)])
+@pytest.mark.parametrize("mode,M,H,k,T", [("fp32", 32, 2, 4, 30), ("bf16", 181, 4, 3, 24),
+                                          ("fp32", 500, 4, 3, 10)])
 def test_stream_with_rotary(mode, M, H, k, T):
     gdt, tdt = DT[mode]
     S, n = 6, 3
