@@ -376,9 +376,10 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     fa = L.gca_frame_attention
     calls = [(t, min(B, T - t)) for t in range(0, T, B)]
     # the kernel that runs the calls (see gca_frame_attention): up to 4 bf16
-    # frames of <= 8 pages one page per wave, more of them held in LDS
+    # frames of <= 8 pages one page per wave, more of them through the
+    # pipelined page loop's frame mode (k_attn_bf16<8, true>)
     ppf = -(-F // 64)
-    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else "k_frame_attn_bf16") if ppf <= 8 else "k_attn_bf16"
+    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else "k_attn_bf16 frame mode") if ppf <= 8 else "k_attn_bf16"
 
     def run():
         for t, nb in calls:
@@ -407,6 +408,9 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     clock = prof["attn_clock_ghz"]
     log(f"{fps:.1f} frames/s; attention {prof['attn_launches']} sampled launches, avg {avg_ms * 1e3:.1f} us, "
         f"{achieved:.1f} TFLOP/s; shader clock {clock:.2f} GHz")
+    phases = phase_summary(prof)
+    if phases:
+        log(f"phase cycles (workgroup 0 of the sampled launches): {json.dumps(phases)}")
     result = {
         "metric": "intra-frame attention frames/s (12 layers, M=500+6, H=16) + % of bf16 MFMA peak",
         "value": round(fps, 2),

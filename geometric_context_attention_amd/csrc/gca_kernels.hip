@@ -326,6 +326,15 @@ static_assert(GCA_SOFT_EXP == 0 || GCA_SOFT_EXP == 4 || GCA_SOFT_EXP == 8, "a qu
 #define GCA_ASYM_ARGS 0
 #endif
 constexpr bool kAsymArgs = GCA_ASYM_ARGS != 0;
+// Intra-frame attention without rotary angles through the pipelined page
+// loop (frame mode of k_attn_bf16) instead of k_frame_attn_bf16.
+#ifndef GCA_FRAME_RING
+#define GCA_FRAME_RING 1
+#endif
+// ... with persistent workgroups when the items outnumber the CUs
+#ifndef GCA_FRAME_PERSIST
+#define GCA_FRAME_PERSIST 1
+#endif
 
 // Phase timing (diagnostic builds, GCA_PHASE_TIMING=1): in workgroup 0 of a
 // sampled launch (AttnArgs::clock set), wave 0 (group A) and wave 4 (group B)
@@ -399,6 +408,37 @@ __device__ __forceinline__ float half_pair_sum(float x) {
 // pass touches (two 128-byte rows per 256 bytes of banks) hit 16 different
 // 16-byte bank groups
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// V tiles of the frame mode are slot-major (row r = slot, 64 d); 16-byte
+// chunk c of slot r sits at chunk position c ^ vswz(r), so that the rows one
+// transposing read takes (see vrow_offsets) fall on different banks
+__device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane 4a+b gets
+// element b of the 8-byte chunks addressed by lanes a, a+4, a+8 and a+12 of
+// its group, in that order
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) uint16_t* lds_u16;
+  typedef __attribute__((address_space(3))) bf16x4* lds_v4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<lds_v4>((lds_u16)(const_cast<uint16_t*>(p))));
+}
+
+// Per-lane element offsets into a slot-major V tile for the PV operand of
+// d-tile dt (v_mfma_f32_32x32x16_bf16 A operand: lane (l32, hf) holds d =
+// 32dt + l32 against the keys of chunk kc that the V^T column order gives:
+// slots swap23(16kc + 8hf + e), e = 0..7).  Two transposing reads, at
+// offset + 1024kc and + 1024kc + 512, give e = 0..3 and 4..7: address lane
+// 4e' + a of a 16-lane group points at slot 16kc + 8r + 4hf + e' (the
+// swap23 image of 16kc + 8hf + 4r + e'), d = 32dt + 16(l32 >> 4) + 4a.
+__device__ __forceinline__ int vrow_offset(int dt, int lane) {
+  const int hf = lane >> 5, g = (lane >> 4) & 1, jl = lane & 15;
+  const int e = jl >> 2, a = jl & 3;
+  const int d0 = dt * 32 + 16 * g + 4 * a;
+  const int slot = hf * 4 + e;  // plus 16kc + 8r, which keep slot & 3
+  return slot * 64 + (((d0 >> 3) ^ vswz(slot)) << 3) + ((d0 >> 2) & 1) * 4;
+}
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding; expcnt and
 // lgkmcnt left at their maxima)
@@ -587,15 +627,55 @@ __device__ __forceinline__ void stage_page(const AttnArgs& a, uint16_t (&ring)[2
   __builtin_amdgcn_global_load_lds(vp, &ring[kRing + slot][wave * 512], 16, 0, 0);
 }
 
+// Frame-mode copy of page j of the frame's own rows (valid slots `valid`)
+// into ring slot `slot`: K as stage_page lays it out, V slot-major (vswz).
+// Slots past the frame's last row repeat that row: their scores are masked,
+// so they only need to be finite.
+__device__ __forceinline__ void stage_frame_page(const AttnArgs& a, uint16_t (&ring)[2 * kRing][kTileElems],
+                                                 int slot, int f, int j, int valid, int h, int tid) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int row = wave * 8 + (lane >> 3), pc = lane & 7;
+  const int r = row < valid ? row : valid - 1;
+  const size_t base = ((size_t)(f * a.Lq + j * kPage + r) * a.H + h) * kHeadDim;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_in) + base + ((pc ^ ((row >> 1) & 7)) << 3);
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_in) + base + ((pc ^ vswz(row)) << 3);
+  __builtin_amdgcn_global_load_lds(kp, &ring[slot][wave * 512], 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(vp, &ring[kRing + slot][wave * 512], 16, 0, 0);
+}
+
+// Copy of the 64 query rows of wave `wave` (rows 64 wave .. +63 of frame f,
+// head h; rows past the frame repeat its last row) into that wave's own LDS
+// tile, laid out as stage_page lays out K (chunk c of row r at c ^ ((r >> 1)
+// & 7)): eight 1 KB copies.
+__device__ __forceinline__ void stage_q_rows(const AttnArgs& a, uint16_t* tile, int f, int h, int wave, int lane) {
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q);
+  // (called inside the page loop: keep the per-lane addresses from being
+  // hoisted out of it into registers)
+  asm volatile("" : "+v"(lane));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = i * 8 + (lane >> 3), pc = lane & 7;
+    int row = wave * 64 + rr;
+    row = row < a.Lq ? row : a.Lq - 1;
+    const uint16_t* src = q + ((size_t)(f * a.Lq + row) * a.H + h) * kHeadDim + ((pc ^ ((rr >> 1) & 7)) << 3);
+    __builtin_amdgcn_global_load_lds(src, tile + i * 512, 16, 0, 0);
+  }
+}
+
 // MFMA phase of page j: QK^T of page j (K from slot sk), the empty slots of
 // its scores masked, then PV of page j-1 (P from the previous VALU phase, V^T
 // from slot sv) with, beside it, the scores turned in place into
 // x = s * c2 - m (c2 = scale * log2 e): the VALU works while the matrix core
 // does, and its work fills the waits on the V operand reads.
-template <int NJ, bool kArgs = true>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int NJ, bool kArgs = true, bool kVRow = false, class AfterV = NoHook>
 __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* sv, const bf16x8 (&qf)[NJ][4],
                                            const bf16x8 (&pf)[NJ][4], f32x16 (&o)[2][NJ], f32x16 (&sc)[2][NJ],
-                                           const float (&m)[NJ], float c2, int valid, int l32, int hf) {
+                                           const float (&m)[NJ], float c2, int valid, int l32, int hf,
+                                           int vo0 = 0, int vo1 = 0, const AfterV& after_v = AfterV{}) {
   if (sk != nullptr) {
     const f32x16 zero = {};
 #pragma unroll
@@ -616,8 +696,15 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
   // PV: V fragment i (kc = i / 2, dt = i % 2) is read two fragments ahead;
   // after each of its MFMAs come four of the 64 multiply-adds, and a
   // scheduling fence after each fragment keeps that order
+  // (kVRow: V slot-major, read transposed at the offsets vrow_offset gives)
   auto vfrag = [&](int i) {
-    return *reinterpret_cast<const bf16x8*>(&sv[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+    if constexpr (kVRow) {
+      const uint16_t* b = sv + ((i % 2) ? vo1 : vo0) + (i / 2) * 1024;
+      const bf16x4 lo = lds_read_tr(b), hi = lds_read_tr(b + 512);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(&sv[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+    }
   };
   bf16x8 vbuf[2] = {vfrag(0), vfrag(1)};
 #pragma unroll
@@ -635,6 +722,11 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
         for (int r = r0; r < r0 + 4; ++r) sc[kt][jq][r] = __builtin_fmaf(sc[kt][jq][r], c2, -m[jq]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // after_v runs once the last V fragment has been read (the transposing
+    // reads wait for every copy in flight: what is issued after them has a
+    // whole page to land)
+    if (i == 5) after_v();
     __builtin_amdgcn_sched_barrier(0);
   }
   if (kArgs && sk != nullptr) {
@@ -763,15 +855,40 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, bf16x8 (&qf)[NJ][4], i
 // lanes per row: the register layout spreads a row over 32 lanes in 8-byte
 // pieces, and storing that directly touches 32 rows per store instruction.
 // The caller makes sure no other wave still reads or fills `stage`.
-template <int NJ>
-__device__ __forceinline__ void attn_epilogue(const AttnArgs& a, const f32x16 (&o)[2][NJ], const float (&m)[NJ],
+// What the epilogue of an attention workgroup writes to: final outputs
+// (nsplit == 1) or the split partials.
+struct EpiArgs {
+  void* out;
+  float* lse;
+  void* part_o;
+  float2* part_ml;
+  int32_t H, Lq, Lq_pad, nsplit;
+  __device__ explicit EpiArgs(const AttnArgs& a)
+      : out(a.out), lse(a.lse), part_o(a.part_o), part_ml(a.part_ml), H(a.H), Lq(a.Lq), Lq_pad(a.Lq_pad),
+        nsplit(a.nsplit) {}
+  // outputs of frame f of a batched launch (bf16 rows)
+  __device__ EpiArgs frame(size_t f) const {
+    EpiArgs e = *this;
+    e.out = static_cast<char*>(out) + f * (size_t)Lq * H * kHeadDim * 2;
+    if (lse != nullptr) e.lse = lse + f * (size_t)H * Lq;
+    return e;
+  }
+};
+
+// kInLoop: called inside a page loop (the persistent frame mode), where
+// only final outputs occur and the lane indices are passed through an empty
+// asm so that the compiler does not hoist the per-lane addresses out of the
+// loop into registers it then has to spill.
+template <int NJ, bool kInLoop = false>
+__device__ __forceinline__ void attn_epilogue(const EpiArgs& a, const f32x16 (&o)[2][NJ], const float (&m)[NJ],
                                               float (&l)[NJ], int h, int qb, int s, int wave, int l32, int hf,
                                               uint16_t* stage) {
   constexpr int D = kHeadDim;
   const int H = a.H;
+  if constexpr (kInLoop) asm volatile("" : "+v"(l32), "+v"(hf));
 #pragma unroll
   for (int j = 0; j < NJ; ++j) l[j] = half_pair_sum(l[j]);
-  const bool final_out = a.nsplit == 1;
+  const bool final_out = kInLoop || a.nsplit == 1;
   const int row0 = qb * kQBlock + wave * 64;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -816,13 +933,12 @@ __device__ __forceinline__ void attn_epilogue(const AttnArgs& a, const f32x16 (&
   }
 }
 
-// Arguments of frame blockIdx.y of a batched intra-frame launch: its rows,
-// outputs, rotary angles and scratch pages follow those of the frames before
-// it (identity for blockIdx.y == 0, i.e. every unbatched launch).
+// Arguments of frame f of a batched intra-frame launch: its rows, outputs,
+// rotary angles and scratch pages follow those of the frames before it
+// (identity for f == 0).
 template <int kElemBytes>
-__device__ __forceinline__ AttnArgs batch_frame(const AttnArgs& in) {
+__device__ __forceinline__ AttnArgs frame_of(const AttnArgs& in, size_t f) {
   AttnArgs a = in;
-  const size_t f = blockIdx.y;
   const size_t rows = (size_t)in.Lq * in.H * kHeadDim * kElemBytes;
   const size_t pages = (size_t)in.pl.ppf * in.H * kPage * kHeadDim * kElemBytes;
   a.q = static_cast<const char*>(in.q) + f * rows;
@@ -836,7 +952,18 @@ __device__ __forceinline__ AttnArgs batch_frame(const AttnArgs& in) {
   return a;
 }
 
-template <int NW>
+// Arguments of frame blockIdx.y (batched launches put frames on grid rows).
+template <int kElemBytes>
+__device__ __forceinline__ AttnArgs batch_frame(const AttnArgs& in) {
+  return frame_of<kElemBytes>(in, blockIdx.y);
+}
+
+// kFrame: intra-frame attention of a batch of frames, one split, every page
+// the frame's own rows (K and V staged from k_in / v_in, V slot-major and
+// read transposed), no rotary angles and no cache bookkeeping.  kPersist
+// (frame mode only): workgroups walk several (frame, head) items each, see
+// below; otherwise one item per workgroup.
+template <int NW, bool kFrame, bool kPersist = false>
 __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   const AttnArgs a = batch_frame<2>(a_in);
   static_assert(NW == 8, "the staging layout assumes 512 threads");
@@ -845,8 +972,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   // One LDS array holds the ring (tiles 0 .. 2*kRing-1) and the page list
   // (the tiles after it): with a single LDS object the compiler can tell the
   // ring slots apart and waits on the copies only where this code asks it to.
+  // (the frame mode has no page list; its tiles after the ring hold each
+  // wave's next query rows)
   constexpr int kListTiles = kListCap * 4 / (kTileElems * 2);
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kRing + kListTiles][kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kRing + (kPersist ? NW : kListTiles)][kTileElems];
   auto& ring = *reinterpret_cast<uint16_t(*)[2 * kRing][kTileElems]>(&lds[0][0]);
   uint32_t* plist = reinterpret_cast<uint32_t*>(&lds[2 * kRing][0]);  // the split's pages, see page_entry
 
@@ -859,35 +988,102 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int H = a.H;
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
-  const int p0 = split_begin(a, s);
-  const int p1 = split_begin(a, s + 1);
-  if (a.pl.fresh_cnt > 0 && a.fresh_frame >= 0 && blockIdx.x == 0) record_fresh_frame(a);
+  // The frame mode is persistent: workgroup w takes the (frame, head) items
+  // w, w + G, w + 2G, ... (G workgroups; item i = frame i / H, head i % H; one
+  // query block per frame) and walks their pages as one list, item after
+  // item, so the ring runs on across items.  At the first page of each item
+  // after the first, a wave loads the item's query rows from its own LDS
+  // tile, writes out the finished item (using that tile as its staging), and
+  // one page later starts the copy of the next item's query rows into it.
+  const int nitems = kPersist ? (a.batch * H - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 1;
+  int fcur = 0;  // frame of the item being walked (frame mode)
+  if constexpr (kFrame) {
+    fcur = (int)blockIdx.x / H;
+    h = (int)blockIdx.x - fcur * H;
+    qb = 0;
+    s = 0;
+  }
+  const int p0 = kFrame ? 0 : split_begin(a, s);
+  const int p1 = kFrame ? nitems * npg : split_begin(a, s + 1);
+  if (!kFrame && a.pl.fresh_cnt > 0 && a.fresh_frame >= 0 && blockIdx.x == 0) record_fresh_frame(a);
   // The prologue issues its loads (the first list entries, Q, the appended
   // frame's rows) before it waits on any of them.
   // The split's pages are resolved once (p1 - p0 <= kListCap: the host picks
   // enough splits); the loop then reads page ids from LDS instead of walking
   // the page tables with scalar code.
-  int valid0;
-  const int raw0 = *page_source(a, p0 + tid < p1 ? p0 + tid : p1 - 1, valid0);
+  int valid0 = 0, raw0 = 0;
+  if constexpr (!kFrame) raw0 = *page_source(a, p0 + tid < p1 ? p0 + tid : p1 - 1, valid0);
 
   bf16x8 qf[NJ][4];
-  load_q<NJ>(a, qf, h, qb, wave, l32, hf);
+  if constexpr (kFrame)
+    load_q<NJ>(frame_of<2>(a, fcur), qf, h, qb, wave, l32, hf);
+  else
+    load_q<NJ>(a, qf, h, qb, wave, l32, hf);
   pc.lap(0);
 
   const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
   const int np = p1 - p0;                // >= 1: there are never more splits than pages
-  if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
-  if (p0 + tid < p1) plist[tid] = page_entry(a, raw0, valid0);
-  for (int i = p0 + tid + NW * 64; i < p1; i += NW * 64) {
-    int valid;
-    const int raw = *page_source(a, i, valid);
-    plist[i - p0] = page_entry(a, raw, valid);
+  if constexpr (!kFrame) {
+    if (a.pl.fresh_cnt > 0) write_fresh_pages(a, ring, p0, p1, h, tid);
+    if (p0 + tid < p1) plist[tid] = page_entry(a, raw0, valid0);
+    for (int i = p0 + tid + NW * 64; i < p1; i += NW * 64) {
+      int valid;
+      const int raw = *page_source(a, i, valid);
+      plist[i - p0] = page_entry(a, raw, valid);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   pc.lap(1);
   // list entry (page id << 7 | valid slots) of split page i, clamped to the
-  // last one (the ring is kept full past the end with copies of that page)
-  auto entry = [&](int i) { return __builtin_amdgcn_readfirstlane(plist[(i < np ? i : np - 1)]); };
+  // last one (the ring is kept full past the end with copies of that page);
+  // in the frame mode the page id is the frame's page index
+  auto entry = [&](int i) -> uint32_t { return __builtin_amdgcn_readfirstlane(plist[i < np ? i : np - 1]); };
+  // The frame mode's entries come from a generator instead, in list order
+  // (the loop asks for them in that order), as frame << 22 | head << 10 |
+  // page << 7 | valid slots, so that no page needs a division.  Items
+  // advance by G = gridDim.x: head by G % H, frame by G / H, with a carry.
+  const int ppf = a.pl.ppf;
+  int g_c = 0, g_j = 0, g_f = fcur, g_h = h, dF = 0, dH = 0;
+  if constexpr (kFrame) {
+    dF = (int)gridDim.x / H;
+    dH = (int)gridDim.x - dF * H;
+  }
+  auto gen = [&]() -> uint32_t {
+    const uint32_t e = ((uint32_t)g_f << 22) | ((uint32_t)g_h << 10) | ((uint32_t)g_j << 7) |
+                       (uint32_t)(g_j == ppf - 1 ? a.pl.f_last_valid : kPage);
+    if (g_c + 1 < np) {  // past the end it keeps giving the last page
+      ++g_c;
+      if (++g_j == ppf) {
+        g_j = 0;
+        g_h += dH;
+        g_f += dF;
+        if (g_h >= H) {
+          g_h -= H;
+          ++g_f;
+        }
+      }
+    }
+    return e;
+  };
+  // frame and head of the workgroup's item k (frame mode; once per item)
+  auto item_frame_head = [&](int k, int& f, int& hh) {
+    const int it = (int)blockIdx.x + k * (int)gridDim.x;
+    f = it / H;
+    hh = it - f * H;
+  };
+  // staging of the page with list entry e into ring slot u
+  auto stage = [&](int u, uint32_t e) {
+    if constexpr (kFrame)
+      stage_frame_page(a, ring, u, (int)(e >> 22), (int)((e >> 7) & 7u), (int)(e & 127u), (int)((e >> 10) & 4095u),
+                       tid);
+    else
+      stage_page(a, ring, u, (int)(e >> 7), h, tid);
+  };
+  uint16_t* const qtile = kPersist ? &lds[2 * kRing + wave][0] : nullptr;  // this wave's next query rows
+  int item = 0;                  // item being walked (frame mode)
+  int item_start = 0;            // its first page
+  int next_start = npg;          // the next item's first page
+  const int vo0 = kFrame ? vrow_offset(0, lane) : 0, vo1 = kFrame ? vrow_offset(1, lane) : 0;
 
   f32x16 o[2][NJ];
 #pragma unroll
@@ -919,7 +1115,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   const bool grp_a = GCA_PINGPONG ? wave < 4 : true;
   // prologue: pages p0 .. p0+kAhead-1 staged, p0 and p0+1 landed; a page
   // this workgroup has just written is only staged after its stores completed
-  if (a.pl.fresh_cnt > 0 && f0 < p1 && f0 - p0 < kAhead) GCA_WAIT_VMCNT(0);
+  if (!kFrame && a.pl.fresh_cnt > 0 && f0 < p1 && f0 - p0 < kAhead) GCA_WAIT_VMCNT(0);
   // V tile of slot kRing-1 (read by the first page's MFMA phase) to zero; no
   // copy writes that slot before the first page's VALU phase
   static_assert(kTileElems * 2 == NW * 64 * 16, "one 16-byte store per thread clears a tile");
@@ -929,10 +1125,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   uint32_t ent[kRing];
 #pragma unroll
   for (int u = 0; u < kAhead; ++u) {
-    ent[u] = entry(u);
-    stage_page(a, ring, u, (int)(ent[u] >> 7), h, tid);
+    ent[u] = kFrame ? gen() : entry(u);
+    stage(u, ent[u]);
   }
-  uint32_t ent_ahead = entry(kAhead);
+  uint32_t ent_ahead = kFrame ? gen() : entry(kAhead);
   GCA_WAIT_VMCNT(2 * (kAhead - 2));
   wg_barrier();
   if (!grp_a) wg_barrier();  // group B runs one phase behind
@@ -958,18 +1154,86 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
       constexpr int SA = (S + kAhead) % kRing;    // slot page p0 + jj + kAhead goes to
       // the entry after that one is read before the MFMA phase's own LDS reads,
       // so it has landed by the time it is used
-      const uint32_t raw_next = plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
-      mfma_phase<NJ, !kA>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
-                          (int)(ent[S] & 127u), l32, hf);
+      const uint32_t raw_next = kFrame ? gen() : plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
+      // frame mode: the first page of an item after the first
+      const bool new_item = kPersist && jj == next_start;
+      // (marked unlikely: the compiler then places it out of the loop's
+      // straight path, which otherwise runs slower beside it)
+      if (__builtin_expect(kPersist && new_item, 0)) {
+        // its query rows (copied one page after the previous boundary)
+        GCA_WAIT_VMCNT(0);
+        int lq = l32, hq = hf;  // addresses computed here, not held across the loop
+        asm volatile("" : "+v"(lq), "+v"(hq));
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            qf[j][c] = *reinterpret_cast<const bf16x8*>(&qtile[swz(j * 32 + lq, c * 2 + hq)]);
+        // the finished item's last PV, then its output (through the tile,
+        // now free); the new item starts from zero O, l and max (this page's
+        // exponent arguments then start from a zero max, as on a
+        // workgroup's first page), and the PV of this page's MFMA phase
+        // multiplies a zero P
+        mfma_phase<NJ, true, true>(nullptr, ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2, kPage,
+                                   l32, hf, vo0, vo1);
+        int f, hh;
+        item_frame_head(item, f, hh);
+        attn_epilogue<NJ, true>(EpiArgs(a).frame(f), o, m, l, hh, 0, 0, wave, l32, hf, qtile);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          m[j] = 0.f;
+          l[j] = 0.f;
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
+        }
+        item += 1;
+        item_start = jj;
+        next_start = jj + npg;
+      }
+      // the copy of the next item's query rows, one page after a boundary
+      const bool q_copy = kPersist && jj == item_start + 1 && item + 1 < nitems;
+      // the frame mode stages page jj + kAhead in this MFMA phase, after its
+      // V reads, into the slot of page jj - 2, which both groups have read
+      // by now (group A in its MFMA phase of page jj - 1, group B one phase
+      // later, before group A's MFMA phase of page jj)
+      auto stage_ahead = [&]() {
+        ent[SA] = ent_ahead;
+        stage(SA, ent_ahead);
+        ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
+        if constexpr (kPersist) {
+          if (__builtin_expect(q_copy, 0)) {
+            int f, hh;
+            item_frame_head(item + 1, f, hh);
+            stage_q_rows(a, qtile, f, hh, wave, lane);
+          }
+        }
+      };
+      if constexpr (kFrame)
+        mfma_phase<NJ, !kA, true>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                                  (int)(ent[S] & 127u), l32, hf, vo0, vo1, stage_ahead);
+      else
+        mfma_phase<NJ, !kA>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                            (int)(ent[S] & 127u), l32, hf);
       pc.lap(3);
       if (GCA_PINGPONG) wg_barrier();
       pc.lap(5);
-      ent[SA] = ent_ahead;
-      stage_page(a, ring, SA, (int)(ent_ahead >> 7), h, tid);
-      ent_ahead = __builtin_amdgcn_readfirstlane(raw_next);
-      valu_phase<NJ, kA>(sc, m, l, o, pf, jj == 0, c2);
+      if constexpr (!kFrame) stage_ahead();
+      valu_phase<NJ, kA>(sc, m, l, o, pf, jj == item_start, c2);
       pc.lap(4);
-      GCA_WAIT_VMCNT(2 * (kAhead - 2));  // this wave's part of page j+2 has landed
+      // this wave's part of page j+2 has landed (in the frame mode the eight
+      // copies of query rows issued on page j or j-1 come after it as well)
+      if (kPersist && (jj == item_start + 1 || jj == item_start + 2) && item + 1 < nitems)
+        GCA_WAIT_VMCNT(2 * (kAhead - 2) + 8);
+      else
+        GCA_WAIT_VMCNT(2 * (kAhead - 2));
       wg_barrier();
       pc.lap(5);
     };
@@ -981,12 +1245,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     run_pages(std::false_type{});
   // PV of the last page; group A then takes the barrier that group B took
   // first, so both have passed the same number
-  mfma_phase<NJ>(nullptr, ring[kRing + (np - 1) % kRing], qf, pf, o, sc, m, c2, kPage, l32, hf);
+  mfma_phase<NJ, true, kFrame>(nullptr, ring[kRing + (np - 1) % kRing], qf, pf, o, sc, m, c2, kPage, l32, hf,
+                               vo0, vo1);
   if (GCA_PINGPONG && grp_a) wg_barrier();
   GCA_WAIT_VMCNT(0);  // no copy into LDS outlives the workgroup
   __syncthreads();    // every wave's copies have landed and its last PV has read the ring
 
-  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf, &ring[wave][0]);
+  if constexpr (kFrame) {
+    int f, hh;
+    item_frame_head(item, f, hh);
+    attn_epilogue<NJ>(EpiArgs(a).frame(f), o, m, l, hh, 0, 0, wave, l32, hf, &ring[wave][0]);
+  } else {
+    attn_epilogue<NJ>(EpiArgs(a), o, m, l, h, qb, s, wave, l32, hf, &ring[wave][0]);
+  }
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
@@ -1113,7 +1384,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   if (grp_a) wg_barrier();
   __syncthreads();  // every wave's last PV has read the tiles
 
-  attn_epilogue<NJ>(a, o, m, l, h, qb, s, wave, l32, hf, &lds[wave][0]);
+  attn_epilogue<NJ>(EpiArgs(a), o, m, l, h, qb, s, wave, l32, hf, &lds[wave][0]);
   if (a.clock != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
     atomicAdd(&a.clock[0], __builtin_amdgcn_s_memtime() - cyc0);
     atomicAdd(&a.clock[1], __builtin_amdgcn_s_memrealtime() - ref0);
@@ -1788,10 +2059,20 @@ hipError_t launch_attention(const AttnArgs& a, bool f32, hipStream_t st) {
                      a.pl.fresh_cnt == a.pl.ppf && a.pl.ppf <= kFrameTiles && a.Lq == a.F && a.nsplit == 1;
   if (f32)
     hipLaunchKernelGGL(k_attn_f32, g3, dim3(256), 0, st, a);
+  else if (frame && a.rope == nullptr && GCA_FRAME_RING && a.batch < 1024) {  // (the frame fits its entry field)
+    // one workgroup per (frame, head) item while they fit the CUs at once;
+    // past that, persistent workgroups, one per CU (items of a single page
+    // keep a workgroup each)
+    const int items = a.H * a.batch;
+    if (a.pl.ppf >= 2 && items > kTargetWgs && GCA_FRAME_PERSIST)
+      hipLaunchKernelGGL((k_attn_bf16<kAttnWaves, true, true>), dim3(kTargetWgs), dim3(kAttnWaves * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_attn_bf16<kAttnWaves, true, false>), dim3(items), dim3(kAttnWaves * 64), 0, st, a);
+  }
   else if (frame)
     hipLaunchKernelGGL(k_frame_attn_bf16, g3, dim3(kAttnWaves * 64), 0, st, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<kAttnWaves>, g3, dim3(kAttnWaves * 64), 0, st, a);
+    hipLaunchKernelGGL((k_attn_bf16<kAttnWaves, false>), g3, dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@ attended within themselves through the C ABI and compared with the fp64
 oracle: bf16 calls of up to 4 frames of up to 8 pages (one page per wave
 of a workgroup, combined in LDS: a lone frame, ragged and full last pages,
 frames with fewer pages than waves, a 7-row frame); longer bf16 calls of up
-to 8 pages per frame (the kernel that holds a frame in LDS, 64 frames per
-launch, so 70 frames make a partial second batch); longer bf16 frames (M = 700: 12 pages, through
+to 8 pages per frame (the pipelined page loop, each workgroup walking one or
+more (frame, head) items in turn; with rotary angles the kernel that holds a
+frame in LDS, 64 frames per launch, so 70 frames make a partial second batch); longer bf16 frames (M = 700: 12 pages, through
 scratch pages, 8 frames per launch at H = 16; the largest frame, 2048 rows); fp32 (64 frames per launch
 at H = 4); and the benchmark's launch, 64 frames of M = 500 at H = 16; the call must leave every layer's cache untouched, so a stream
 interleaving frame attention with GCA steps still matches the oracle and its
@@ -34,7 +35,12 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
                                          ("bf16", 120, 4, 70), ("bf16", 700, 16, 10), ("bf16", 500, 16, 64),
                                          ("bf16", 181, 4, 2), ("bf16", 58, 2, 4), ("bf16", 506, 16, 1),
                                          ("bf16", 1, 2, 3), ("bf16", 250, 8, 4), ("bf16", 500, 16, 5),
-                                         ("bf16", 2042, 2, 3), ("fp32", 2042, 1, 2)])
+                                         ("bf16", 2042, 2, 3), ("fp32", 2042, 1, 2),
+                                         # the pipelined frame loop at one page: 7 rows, a full page
+                                         ("bf16", 1, 2, 9), ("bf16", 58, 2, 6), ("bf16", 122, 4, 8),
+                                         # several (frame, head) items per workgroup: two full pages,
+                                         # three with a ragged last one
+                                         ("bf16", 122, 16, 64), ("bf16", 181, 8, 100)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6
