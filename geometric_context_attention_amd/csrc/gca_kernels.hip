@@ -1144,6 +1144,45 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
+  // Frame mode, the switch to the workgroup's next item, whose first page is
+  // `first`: the finished item's last PV (P of the page before `first`, V
+  // tile `sv`), its output (through this wave's tile, free once the new
+  // item's query rows have been read from it), then zero O, l, max and P
+  // (the new item's first exponent arguments start from a zero max, as on
+  // a workgroup's first page, and the PV of that page's MFMA phase
+  // multiplies the zero P).
+  auto switch_item = [&](const uint16_t* sv, int first) __attribute__((always_inline)) {
+    GCA_WAIT_VMCNT(0);  // the query rows, copied one page after the last switch
+    int lq = l32, hq = hf;  // addresses computed here, not held across the loop
+    asm volatile("" : "+v"(lq), "+v"(hq));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        qf[j][c] = *reinterpret_cast<const bf16x8*>(&qtile[swz(j * 32 + lq, c * 2 + hq)]);
+    mfma_phase<NJ, true, true>(nullptr, sv, qf, pf, o, sc, m, c2, kPage, l32, hf, vo0, vo1);
+    int f, hh;
+    item_frame_head(item, f, hh);
+    attn_epilogue<NJ, true>(EpiArgs(a).frame(f), o, m, l, hh, 0, 0, wave, l32, hf, qtile);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      m[j] = 0.f;
+      l[j] = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
+    }
+    item += 1;
+    item_start = first;
+    next_start = first + npg;
+  };
   // the page loop; kA: this wave computes its exponent arguments in its
   // softmax phase (group A of the asymmetric variant), else beside its MFMAs.
   // The two kinds of wave run separate copies of the loop.
@@ -1155,49 +1194,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
       // the entry after that one is read before the MFMA phase's own LDS reads,
       // so it has landed by the time it is used
       const uint32_t raw_next = kFrame ? gen() : plist[jj + kAhead + 1 < np ? jj + kAhead + 1 : np - 1];
-      // frame mode: the first page of an item after the first
+      // frame mode: the first page of an item after the first.  Group A
+      // switches items at the start of that page (its MFMA phase), group B
+      // at the end of the page before (its softmax phase, the same global
+      // phase), so the two switches overlap.
       const bool new_item = kPersist && jj == next_start;
-      // (marked unlikely: the compiler then places it out of the loop's
-      // straight path, which otherwise runs slower beside it)
-      if (__builtin_expect(kPersist && new_item, 0)) {
-        // its query rows (copied one page after the previous boundary)
-        GCA_WAIT_VMCNT(0);
-        int lq = l32, hq = hf;  // addresses computed here, not held across the loop
-        asm volatile("" : "+v"(lq), "+v"(hq));
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            qf[j][c] = *reinterpret_cast<const bf16x8*>(&qtile[swz(j * 32 + lq, c * 2 + hq)]);
-        // the finished item's last PV, then its output (through the tile,
-        // now free); the new item starts from zero O, l and max (this page's
-        // exponent arguments then start from a zero max, as on a
-        // workgroup's first page), and the PV of this page's MFMA phase
-        // multiplies a zero P
-        mfma_phase<NJ, true, true>(nullptr, ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2, kPage,
-                                   l32, hf, vo0, vo1);
-        int f, hh;
-        item_frame_head(item, f, hh);
-        attn_epilogue<NJ, true>(EpiArgs(a).frame(f), o, m, l, hh, 0, 0, wave, l32, hf, qtile);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          m[j] = 0.f;
-          l[j] = 0.f;
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pf[j][kc][e] = (__bf16)0.f;
-        }
-        item += 1;
-        item_start = jj;
-        next_start = jj + npg;
-      }
+      if (__builtin_expect(kPersist && new_item && grp_a, 0)) switch_item(ring[kRing + (S + kRing - 1) % kRing], jj);
       // the copy of the next item's query rows, one page after a boundary
       const bool q_copy = kPersist && jj == item_start + 1 && item + 1 < nitems;
       // the frame mode stages page jj + kAhead in this MFMA phase, after its
@@ -1227,6 +1229,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
       pc.lap(5);
       if constexpr (!kFrame) stage_ahead();
       valu_phase<NJ, kA>(sc, m, l, o, pf, jj == item_start, c2);
+      if (__builtin_expect(kPersist && !grp_a && jj + 1 == next_start && item + 1 < nitems, 0))
+        switch_item(ring[kRing + S], jj + 1);
       pc.lap(4);
       // this wave's part of page j+2 has landed (in the frame mode the eight
       // copies of query rows issued on page j or j-1 come after it as well)
