@@ -335,6 +335,11 @@ constexpr bool kAsymArgs = GCA_ASYM_ARGS != 0;
 #ifndef GCA_FRAME_PERSIST
 #define GCA_FRAME_PERSIST 1
 #endif
+// 1: the stream loop also issues page j+kAhead's copy in page j's MFMA phase,
+// after its V reads (as the frame mode must), instead of in its softmax phase
+#ifndef GCA_STAGE_MFMA
+#define GCA_STAGE_MFMA 0
+#endif
 
 // Phase timing (diagnostic builds, GCA_PHASE_TIMING=1): in workgroup 0 of a
 // sampled launch (AttnArgs::clock set), wave 0 (group A) and wave 4 (group B)
@@ -1221,13 +1226,16 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
       if constexpr (kFrame)
         mfma_phase<NJ, !kA, true>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
                                   (int)(ent[S] & 127u), l32, hf, vo0, vo1, stage_ahead);
+      else if constexpr (GCA_STAGE_MFMA != 0)
+        mfma_phase<NJ, !kA, false>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                                   (int)(ent[S] & 127u), l32, hf, 0, 0, stage_ahead);
       else
         mfma_phase<NJ, !kA>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
                             (int)(ent[S] & 127u), l32, hf);
       pc.lap(3);
       if (GCA_PINGPONG) wg_barrier();
       pc.lap(5);
-      if constexpr (!kFrame) stage_ahead();
+      if constexpr (!kFrame && GCA_STAGE_MFMA == 0) stage_ahead();
       valu_phase<NJ, kA>(sc, m, l, o, pf, jj == item_start, c2);
       if (__builtin_expect(kPersist && !grp_a && jj + 1 == next_start && item + 1 < nitems, 0))
         switch_item(ring[kRing + S], jj + 1);
