@@ -993,13 +993,13 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   const unsigned long long cyc0 = __builtin_amdgcn_s_memtime(), ref0 = __builtin_amdgcn_s_memrealtime();
   const int H = a.H;
   const int npg = a.pl.a_cnt + a.pl.s_cnt + a.pl.w_cnt + a.pl.fresh_cnt;
-  // The frame mode is persistent: workgroup w takes the (frame, head) items
-  // w, w + G, w + 2G, ... (G workgroups; item i = frame i / H, head i % H; one
-  // query block per frame) and walks their pages as one list, item after
-  // item, so the ring runs on across items.  At the first page of each item
-  // after the first, a wave loads the item's query rows from its own LDS
-  // tile, writes out the finished item (using that tile as its staging), and
-  // one page later starts the copy of the next item's query rows into it.
+  // Frame mode: workgroup w takes the (frame, head) items w, w + G, w + 2G,
+  // ... (G workgroups; item i = frame i / H, head i % H; one query block per
+  // frame).  Persistent (kPersist), it walks their pages as one list, item
+  // after item, so the ring runs on across items: at each switch (see
+  // switch_item) a wave loads the next item's query rows from its own LDS
+  // tile and writes out the finished item through that tile, and one page
+  // into the new item it starts copying the following item's rows there.
   const int nitems = kPersist ? (a.batch * H - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 1;
   int fcur = 0;  // frame of the item being walked (frame mode)
   if constexpr (kFrame) {
