@@ -340,6 +340,11 @@ constexpr bool kAsymArgs = GCA_ASYM_ARGS != 0;
 #ifndef GCA_STAGE_MFMA
 #define GCA_STAGE_MFMA 0
 #endif
+// k_frame_wsplit_bf16: V copied slot-major and read transposed (1) or
+// transposed through registers (0)
+#ifndef GCA_WS_VROW
+#define GCA_WS_VROW 1
+#endif
 
 // Phase timing (diagnostic builds, GCA_PHASE_TIMING=1): in workgroup 0 of a
 // sampled launch (AttnArgs::clock set), wave 0 (group A) and wave 4 (group B)
@@ -614,6 +619,14 @@ template <class RowPtr>
 __device__ __forceinline__ void copy_rows8(uint16_t* tile, int r0, int lane, RowPtr src_row) {
   const int r = r0 + (lane >> 3), pc = lane & 7;
   __builtin_amdgcn_global_load_lds(src_row(r) + ((pc ^ ((r >> 1) & 7)) << 3), tile + r0 * kHeadDim, 16, 0, 0);
+}
+
+// The same for a slot-major V tile (chunk c of row r at c ^ vswz(r), read
+// back with the transposing LDS read at the offsets vrow_offset gives).
+template <class RowPtr>
+__device__ __forceinline__ void copy_vrows8(uint16_t* tile, int r0, int lane, RowPtr src_row) {
+  const int r = r0 + (lane >> 3), pc = lane & 7;
+  __builtin_amdgcn_global_load_lds(src_row(r) + ((pc ^ vswz(r)) << 3), tile + r0 * kHeadDim, 16, 0, 0);
 }
 
 // Issue the copy of physical page pg into ring slot `slot` (K and V tiles):
@@ -1407,8 +1420,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
 // one workgroup per (frame, head, 32-row query block), wave w takes page w
 // of the frame (keys 64w .. 64w+63).  The Q block and each wave's K page are
 // copied into swizzled LDS tiles with full-row (coalesced) copies; each wave
-// transposes its V page into an LDS tile of its own, then computes its
-// page's scores, their softmax against its own row max and the PV product.
+// copies its V page slot-major into an LDS tile of its own and reads it with
+// the transposing LDS read (GCA_WS_VROW=0: transposes it through registers
+// instead), then computes its page's scores, their softmax against its own
+// row max and the PV product.
 // The waves' (m, l, O) are combined in LDS in fp32.  Nothing passes through
 // memory between these steps and there is no merge launch, so a lone frame
 // costs one short launch: the latency-bound case (one frame per call) that
@@ -1457,7 +1472,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
     });
   uint4 vr[8];
   const int cg = lane >> 3, ch = lane & 7;
-  if (valid > 0) {  // uniform
+  if (valid > 0 && GCA_WS_VROW) {  // uniform; rows past the valid ones repeat the last (P is 0 there)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      copy_rows8(kt_of(wave), i * 8, lane, [&](int r) {
+        return kin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
+      });
+      copy_vrows8(vt_of(wave), i * 8, lane, [&](int r) {
+        return vin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
+      });
+    }
+  } else if (valid > 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       copy_rows8(kt_of(wave), i * 8, lane, [&](int r) {
@@ -1548,9 +1573,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
     lrow = half_pair_sum(acc);
     // O^T += V^T P^T: fragment i is d-tile i % 2, 16-key chunk i / 2
     const uint16_t* vt = vt_of(wave);
+    const int vo[2] = {vrow_offset(0, lane), vrow_offset(1, lane)};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&vt[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+      bf16x8 vf;
+      if constexpr (GCA_WS_VROW != 0) {
+        const uint16_t* b = vt + vo[i % 2] + (i / 2) * 1024;
+        vf = __builtin_shufflevector(lds_read_tr(b), lds_read_tr(b + 512), 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        vf = *reinterpret_cast<const bf16x8*>(&vt[swz((i % 2) * 32 + l32, (i / 2) * 2 + hf)]);
+      }
       o[i % 2][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[0][i / 2], o[i % 2][0], 0, 0, 0);
     }
   }
