@@ -375,11 +375,16 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     sp = ctypes.c_void_p(stream.cuda_stream)
     fa = L.gca_frame_attention
     calls = [(t, min(B, T - t)) for t in range(0, T, B)]
+    if args.rotary:  # one call's frames of angles, resident for the whole run
+        from geometric_context_attention_amd.synth import rotary_table
+        tab = rotary_table(0, B, F, S, D).to(dev).reshape(B * F, D // 2, 2).contiguous()
+        G.gca_set_rotary(ctx, tab)
     # the kernel that runs the calls (see gca_frame_attention): up to 4 bf16
     # frames of <= 8 pages one page per wave, more of them through the
     # pipelined page loop's frame mode (k_attn_bf16<8, true>)
     ppf = -(-F // 64)
-    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else "k_attn_bf16 frame mode") if ppf <= 8 else "k_attn_bf16"
+    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else ("k_frame_attn_bf16" if args.rotary else "k_attn_bf16 frame mode")
+                    if ppf <= 8 else "k_attn_bf16")
 
     def run():
         for t, nb in calls:
@@ -425,7 +430,8 @@ def frame_attention_bench(args, cfg, G, torch, dev):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), resident pool of frames per layer)",
         "config": {"workload": f"intra-frame attention: {Ly} layers, H={H}, D={D}, M={M}+{S}, T={T} frames, "
-                               f"{B} frames per call, bf16", "frames_per_call": B},
+                               f"{B} frames per call, bf16" + (", rotary Q/K" if args.rotary else ""),
+                   "frames_per_call": B},
         "roofline": {
             "bound": "mfma",
             "kernel": frame_kernel,

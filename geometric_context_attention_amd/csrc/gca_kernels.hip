@@ -1295,8 +1295,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
 }
 
 // Intra-frame attention of one (frame, head) per workgroup, the frame at most
-// kFrameTiles pages long: its K tiles and V^T tiles are built once in LDS from
-// the input rows (rotated keys when rotary angles are given), so the page loop
+// kFrameTiles pages long (the calls with rotary angles; the others run in the
+// frame mode of k_attn_bf16): its rotated K tiles are built once in LDS from
+// the input rows and its V pages copied there slot-major, so the page loop
 // reads no memory.  The loop is the ping-pong of the stream kernel without the
 // copies.  Launches batch frames on grid rows and run one split (final
 // outputs).
@@ -1316,21 +1317,24 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   bf16x8 qf[NJ][4];
   load_q<NJ>(a, qf, h, qb, wave, l32, hf);
 
-  // K row r, chunk c of page j at swz(r, c) of tile j; V^T element (d, col)
-  // (col = swap23(slot), as in the pool) at swz(d, col / 8) + col % 8 of tile
-  // kFrameTiles + j; empty slots are zero
+  // K row r, chunk c of page j at swz(r, c) of tile j (rotated, empty slots
+  // zero); V slot-major in tile kFrameTiles + j (chunk c of slot r at
+  // c ^ vswz(r); slots past the frame repeat its last row, where P is 0),
+  // copied straight into LDS by wave j and read with the transposing read
   {
     const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
     const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
     const int row = tid >> 3, ch = tid & 7;  // K: one 16-byte chunk of each tile per thread
-    // V: wave w transposes page w of the split; lane (cg, ch) = (lane >> 3,
-    // lane & 7) fills V^T chunk cg (columns 8cg .. 8cg+7) of rows d = 8ch ..
-    // 8ch+7.  Column 8cg + i holds slot swap23(8cg + i) = 16(cg >> 1) +
-    // 8(i >> 2) + 4(cg & 1) + i % 4, whose 16-byte chunk ch it loads.
-    const int cg = lane >> 3;
     const int vpj = p0 + wave;
     const int vvalid = wave < np ? ((vpj == ppf - 1) ? a.pl.f_last_valid : kPage) : 0;
-    uint4 kv[kFrameTiles], vr[8];
+    if (vvalid > 0) {  // uniform
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        copy_vrows8(&lds[kFrameTiles + wave][0], i * 8, lane, [&](int r) {
+          return vin + ((size_t)(vpj * kPage + min(r, vvalid - 1)) * a.H + h) * kHeadDim;
+        });
+    }
+    uint4 kv[kFrameTiles];
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
       const int pj = p0 + j;  // page of the frame
@@ -1338,13 +1342,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
       kv[j] = make_uint4(0u, 0u, 0u, 0u);
       if (j < np && row < valid)
         kv[j] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pj * kPage + row) * a.H + h) * kHeadDim + ch * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int slot = 16 * (cg >> 1) + 8 * (i >> 2) + 4 * (cg & 1) + (i & 3);
-      vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (slot < vvalid)
-        vr[i] = *reinterpret_cast<const uint4*>(vin + ((size_t)(vpj * kPage + slot) * a.H + h) * kHeadDim + ch * 8);
     }
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
@@ -1356,22 +1353,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
         *reinterpret_cast<uint4*>(&lds[j][swz(row, ch)]) = kv[j];
       }
     }
-    if (wave < np) {  // uniform
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t wd[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x0 = (&vr[2 * w].x)[e >> 1], x1 = (&vr[2 * w + 1].x)[e >> 1];
-          wd[w] = (e & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        }
-        *reinterpret_cast<uint4*>(&lds[kFrameTiles + wave][swz(ch * 8 + e, cg)]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
-      }
-    }
     static_assert(kTileElems * 2 == kAttnWaves * 64 * 16, "one 16-byte store per thread clears a tile");
     *reinterpret_cast<uint4*>(&lds[2 * kFrameTiles][tid * 8]) = make_uint4(0u, 0u, 0u, 0u);
   }
+  GCA_WAIT_VMCNT(0);  // this wave's V copies have landed
   __syncthreads();
+  const int vo0 = vrow_offset(0, lane), vo1 = vrow_offset(1, lane);
 
   f32x16 o[2][NJ];
 #pragma unroll
@@ -1399,13 +1386,13 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   if (!grp_a) wg_barrier();
   for (int jj = 0; jj < np; ++jj) {
     const int valid = (p0 + jj == ppf - 1) ? a.pl.f_last_valid : kPage;
-    mfma_phase<NJ>(lds[jj], lds[jj == 0 ? 2 * kFrameTiles : kFrameTiles + jj - 1], qf, pf, o, sc, m, c2, valid,
-                   l32, hf);
+    mfma_phase<NJ, true, true>(lds[jj], lds[jj == 0 ? 2 * kFrameTiles : kFrameTiles + jj - 1], qf, pf, o, sc, m, c2,
+                               valid, l32, hf, vo0, vo1);
     wg_barrier();
     valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
     wg_barrier();
   }
-  mfma_phase<NJ>(nullptr, lds[kFrameTiles + np - 1], qf, pf, o, sc, m, c2, kPage, l32, hf);
+  mfma_phase<NJ, true, true>(nullptr, lds[kFrameTiles + np - 1], qf, pf, o, sc, m, c2, kPage, l32, hf, vo0, vo1);
   if (grp_a) wg_barrier();
   __syncthreads();  // every wave's last PV has read the tiles
 

@@ -69,9 +69,10 @@ def test_stream_with_rotary(mode, M, H, k, T):
     stack.close()
 
 
-@pytest.mark.parametrize("mode,B", [("bf16", 3), ("bf16", 6), ("fp32", 3)])
+@pytest.mark.parametrize("mode,B", [("bf16", 3), ("bf16", 6), ("bf16", 70), ("fp32", 3)])
 def test_frame_attention_with_rotary(mode, B):
-    """3 bf16 frames: one page per wave; 6: each frame held in LDS; fp32: scratch pages."""
+    """3 bf16 frames: one page per wave; 6 and 70 (a full launch of 64 frames,
+    then 6): each frame held in LDS; fp32: scratch pages."""
     gdt, tdt = DT[mode]
     M, S, H = 250, 6, 4
     F = M + S
