@@ -40,7 +40,10 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
                                          ("bf16", 1, 2, 9), ("bf16", 58, 2, 6), ("bf16", 122, 4, 8),
                                          # several (frame, head) items per workgroup: two full pages,
                                          # three with a ragged last one
-                                         ("bf16", 122, 16, 64), ("bf16", 181, 8, 100)])
+                                         ("bf16", 122, 16, 64), ("bf16", 181, 8, 100),
+                                         # head counts that do not divide the 256 workgroups, so that
+                                         # stepping to a workgroup's next item carries into the frame
+                                         ("bf16", 122, 12, 30), ("bf16", 122, 3, 100), ("bf16", 500, 12, 64)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6
