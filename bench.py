@@ -416,8 +416,20 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     phases = phase_summary(prof)
     if phases:
         log(f"phase cycles (workgroup 0 of the sampled launches): {json.dumps(phases)}")
+    # Algorithmic bytes: every frame's Q, K and V read once and O written once
+    # (no LSE here), i.e. twice the K/V bytes the profile counts.  At
+    # head_dim 64 and M+S = 506 that is 251 flop/byte, below the ridge of the
+    # bf16 peak over HBM (312.5 flop/byte): the roofline that bounds these
+    # layers is HBM, and the MFMA fraction is reported beside it.
+    launches = max(prof["attn_launches"], 1)
+    io_bytes = 2.0 * prof["attn_kv_bytes"]
+    intensity = prof["attn_flop"] / io_bytes if io_bytes > 0 else 0.0
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    gbs = io_bytes / (prof["attn_ms"] * 1e-3) / 1e9 if prof["attn_ms"] > 0 else 0.0
+    hbm_bound = intensity < ridge
+    attainable = min(PEAK_BF16_TFLOPS, PEAK_HBM_GBS * intensity / 1e3)
     result = {
-        "metric": "intra-frame attention frames/s (12 layers, M=500+6, H=16) + % of bf16 MFMA peak",
+        "metric": "intra-frame attention frames/s (12 layers, M=500+6, H=16) + % of the roofline",
         "value": round(fps, 2),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -433,16 +445,21 @@ def frame_attention_bench(args, cfg, G, torch, dev):
                                f"{B} frames per call, bf16" + (", rotary Q/K" if args.rotary else ""),
                    "frames_per_call": B},
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm" if hbm_bound else "mfma",
             "kernel": frame_kernel,
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "achieved": round(gbs, 1) if hbm_bound else round(achieved, 2),
+            "peak": PEAK_HBM_GBS if hbm_bound else PEAK_BF16_TFLOPS,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4) if hbm_bound else round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "sampled_launches": prof["attn_launches"],
-            "algorithmic_flop_per_launch": prof["attn_flop"] / max(prof["attn_launches"], 1),
+            "algorithmic_flop_per_launch": prof["attn_flop"] / launches,
+            "algorithmic_bytes_per_launch": io_bytes / launches,
+            "arithmetic_intensity_flop_per_byte": round(intensity, 1),
+            "tflops": round(achieved, 2),
+            "frac_of_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac_of_attainable": round(achieved / attainable, 4) if attainable > 0 else None,
             "clock_ghz": round(clock, 3),
             "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
         },
