@@ -43,7 +43,9 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
                                          ("bf16", 122, 16, 64), ("bf16", 181, 8, 100),
                                          # head counts that do not divide the 256 workgroups, so that
                                          # stepping to a workgroup's next item carries into the frame
-                                         ("bf16", 122, 12, 30), ("bf16", 122, 3, 100), ("bf16", 500, 12, 64)])
+                                         ("bf16", 122, 12, 30), ("bf16", 122, 3, 100), ("bf16", 500, 12, 64),
+                                         # frames of exactly 8 full pages, walked by persistent workgroups
+                                         ("bf16", 506, 4, 70)])
 def test_frame_attention_matches_oracle(mode, M, H, B):
     gdt, tdt = DT[mode]
     S = 6
@@ -56,6 +58,24 @@ def test_frame_attention_matches_oracle(mode, M, H, B):
     o_ref, l_ref = go.frame_attention(to64(q), to64(k), to64(v), 1 / math.sqrt(64))
     ma, rel = check_outputs(out, o_ref, lse, l_ref, mode, f"frame attention {mode} M={M} B={B}")
     say(f"  frame attention {mode} M={M} H={H} B={B}: max-abs {ma:.2e} rel {rel:.2e}")
+    stack.close()
+
+
+@pytest.mark.parametrize("M,H,B", [(500, 16, 64), (500, 16, 16), (500, 16, 2), (181, 4, 70)])
+def test_frame_attention_without_lse(M, H, B):
+    """No LSE buffer (as the benchmark calls it): the outputs are the same
+    bits as with one, on every kernel that serves bf16 calls."""
+    S = 6
+    cfg = G.make_config(num_heads=H, image_tokens=M, summary_tokens=S, n_anchor=3, k_window=4,
+                        max_frames=16, dtype=G.GCA_BF16)
+    stack = G.GcaStack(cfg)
+    spec = StreamSpec(H=H, D=64, M=M, S=S, dtype=torch.bfloat16, seed=13, chunk=16)
+    q, k, v = (t.cuda() for t in draw_frames(spec, 0, 0, B))
+    with_lse, _ = stack.frame_attention(q, k, v)
+    without, lse = stack.frame_attention(q, k, v, want_lse=False)
+    assert lse is None
+    assert torch.equal(with_lse.view(torch.int16), without.view(torch.int16))
+    say(f"  frame attention without LSE M={M} H={H} B={B}: bit-identical")
     stack.close()
 
 
