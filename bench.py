@@ -356,6 +356,7 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     """The intra-frame layers: every frame's M+S tokens attend among
     themselves, in each of the layers, gca_frame_attention taking
     --frames-per-call frames per call (1 = streaming, one frame per step)."""
+    from geometric_context_attention_amd.profiling import FRAME_TRAFFIC_FILE, read_traffic
     from geometric_context_attention_amd.synth import StreamSpec, draw_frames
 
     H, D, M, S, Ly, T = cfg.num_heads, cfg.head_dim, cfg.image_tokens, cfg.summary_tokens, cfg.num_layers, args.frames
@@ -451,7 +452,8 @@ def frame_attention_bench(args, cfg, G, torch, dev):
             "peak": PEAK_HBM_GBS if hbm_bound else PEAK_BF16_TFLOPS,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4) if hbm_bound else round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (read_traffic(FRAME_TRAFFIC_FILE)
+                        if (B, T, Ly, H, M, S) == (64, 2048, 12, 16, 500, 6) and not args.rotary else None),
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "sampled_launches": prof["attn_launches"],
             "algorithmic_flop_per_launch": prof["attn_flop"] / launches,

@@ -24,6 +24,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(PKG, "csrc", "gca_kernels.hip")
 TRAFFIC_FILE = os.path.join(os.path.dirname(PKG), "profiles", "k_attn_bf16_gca_stream_traffic.txt")
+# the same for the intra-frame layers at 64 frames per call (frame mode)
+FRAME_TRAFFIC_FILE = os.path.join(os.path.dirname(PKG), "profiles",
+                                  "k_attn_bf16_frame_mode_intra_frame_64_per_call_traffic.txt")
 
 
 def kernel_source_digest() -> str:
@@ -84,7 +87,8 @@ def counter_total(path: str, kernel: str, counter: str) -> float:
 
 
 def traffic_report(fetch_csv: str, write_csv: str, cal_fetch_csv: str, cal_write_csv: str, kernel: str,
-                   kv_bytes: float, cal_read: float, cal_written: float, workload: str, commands) -> str:
+                   kv_bytes: float, cal_read: float, cal_written: float, workload: str, commands,
+                   read_label: str = "K/V") -> str:
     """Calibrated HBM bytes per dispatch of `kernel` from two ``--pmc`` runs
     (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the same
     counter reads for the copy calibration (``bench.py --copy-calibration``:
@@ -104,7 +108,7 @@ def traffic_report(fetch_csv: str, write_csv: str, cal_fetch_csv: str, cal_write
             f"# Raw (KiB per dispatch): FETCH_SIZE {f:.1f}, WRITE_SIZE {w:.1f}",
             f"# Calibration (elementwise copy kernels): FETCH_SIZE {cf:.6g} KiB for {cal_read:.6g} B read,",
             f"#   WRITE_SIZE {cw:.6g} KiB for {cal_written:.6g} B written => scale x{sf:.4f} / x{sw:.4f}",
-            f"# Algorithmic K/V bytes per launch: {kv_bytes:.6g}; calibrated fetch is {fb / kv_bytes:.3f}x that",
+            f"# Algorithmic {read_label} bytes per launch: {kv_bytes:.6g}; calibrated fetch is {fb / kv_bytes:.3f}x that",
             "", f"kernel_source_sha256: {kernel_source_digest()}",
             f"fetch_bytes_per_launch: {fb:.6g}", f"write_bytes_per_launch: {wb:.6g}",
             f"hbm_bytes_per_launch: {fb + wb:.6g}"]
@@ -149,7 +153,8 @@ def main(argv=None):
     for name in ("fetch", "write", "cal_fetch", "cal_write"):
         r.add_argument("--" + name.replace("_", "-"), required=True)
     r.add_argument("--kernel", default="k_attn_bf16")
-    r.add_argument("--kv-bytes", type=float, required=True, help="algorithmic K/V bytes per launch")
+    r.add_argument("--kv-bytes", type=float, required=True, help="algorithmic bytes read per launch")
+    r.add_argument("--read-label", default="K/V", help="what those bytes are, for the report")
     r.add_argument("--cal-read", type=float, required=True)
     r.add_argument("--cal-written", type=float, required=True)
     r.add_argument("--workload", required=True)
@@ -159,7 +164,8 @@ def main(argv=None):
     if args.cmd == "traffic-report":
         with open(args.out, "w") as fh:
             fh.write(traffic_report(args.fetch, args.write, args.cal_fetch, args.cal_write, args.kernel,
-                                    args.kv_bytes, args.cal_read, args.cal_written, args.workload, args.command))
+                                    args.kv_bytes, args.cal_read, args.cal_written, args.workload, args.command,
+                                    args.read_label))
         return 0
     if args.cmd == "trace-report":
         line = None
