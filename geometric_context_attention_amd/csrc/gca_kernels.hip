@@ -1315,7 +1315,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
   const int ppf = a.pl.ppf;  // <= kFrameTiles (checked at launch)
   const int p0 = 0, np = ppf;  // one split: every page of the frame
   bf16x8 qf[NJ][4];
-  load_q<NJ>(a, qf, h, qb, wave, l32, hf);
 
   // K row r, chunk c of page j at swz(r, c) of tile j (rotated, empty slots
   // zero); V slot-major in tile kFrameTiles + j (chunk c of slot r at
@@ -1325,31 +1324,78 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
     const uint16_t* kin = reinterpret_cast<const uint16_t*>(a.k_in);
     const uint16_t* vin = reinterpret_cast<const uint16_t*>(a.v_in);
     const int row = tid >> 3, ch = tid & 7;  // K: one 16-byte chunk of each tile per thread
-    const int vpj = p0 + wave;
-    const int vvalid = wave < np ? ((vpj == ppf - 1) ? a.pl.f_last_valid : kPage) : 0;
-    if (vvalid > 0) {  // uniform
+    // Every load of the prologue is issued before any is used, and without
+    // branches, so that the rotations wait for the loads they need and not
+    // for the V copies issued last: query rows past the frame, pages past the
+    // frame's and rows past a page's valid ones read the last row, and waves
+    // past the frame's pages copy its last page into their V tile, which is
+    // never read.  The Q fragments are the ones load_q reads.
+    uint4 qv[NJ][4];
+    float2 qcs[NJ][4][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int qrow = min(qb * kQBlock + wave * 64 + j * 32 + l32, a.Lq - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        qv[j][c] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.q) +
+                                                   ((size_t)qrow * a.H + h) * kHeadDim + c * 16 + hf * 8);
+    }
+    if (a.rope != nullptr) {  // uniform
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int qrow = min(qb * kQBlock + wave * 64 + j * 32 + l32, a.Lq - 1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qcs[j][c][e] = a.rope[(size_t)qrow * (kHeadDim / 2) + c * 8 + hf * 4 + e];
+      }
+    }
+    uint4 kv[kFrameTiles];
+    float2 cs[kFrameTiles][4];
+#pragma unroll
+    for (int j = 0; j < kFrameTiles; ++j) {
+      const int pj = min(p0 + j, ppf - 1);
+      const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
+      kv[j] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pj * kPage + min(row, valid - 1)) * a.H + h) * kHeadDim + ch * 8);
+    }
+    if (a.rope != nullptr) {  // uniform
+#pragma unroll
+      for (int j = 0; j < kFrameTiles; ++j) {
+        const int pj = min(p0 + j, ppf - 1);
+        const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
+        const float2* t = a.rope + (size_t)(pj * kPage + min(row, valid - 1)) * (kHeadDim / 2) + ch * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[j][e] = t[e];
+      }
+    }
+    {
+      const int vpj = min(p0 + wave, ppf - 1);
+      const int vvalid = (vpj == ppf - 1) ? a.pl.f_last_valid : kPage;
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         copy_vrows8(&lds[kFrameTiles + wave][0], i * 8, lane, [&](int r) {
           return vin + ((size_t)(vpj * kPage + min(r, vvalid - 1)) * a.H + h) * kHeadDim;
         });
     }
-    uint4 kv[kFrameTiles];
 #pragma unroll
-    for (int j = 0; j < kFrameTiles; ++j) {
-      const int pj = p0 + j;  // page of the frame
-      const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
-      kv[j] = make_uint4(0u, 0u, 0u, 0u);
-      if (j < np && row < valid)
-        kv[j] = *reinterpret_cast<const uint4*>(kin + ((size_t)(pj * kPage + row) * a.H + h) * kHeadDim + ch * 8);
+    for (int j = 0; j < NJ; ++j) {
+      const bool in = qb * kQBlock + wave * 64 + j * 32 + l32 < a.Lq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (in) v = a.rope != nullptr ? rope_bf16x8(qv[j][c], qcs[j][c]) : qv[j][c];
+        qf[j][c] = __builtin_bit_cast(bf16x8, v);
+      }
     }
 #pragma unroll
     for (int j = 0; j < kFrameTiles; ++j) {
       if (j < np) {
         const int pj = p0 + j;
         const int valid = (pj == ppf - 1) ? a.pl.f_last_valid : kPage;
-        if (a.rope != nullptr && row < valid)
-          kv[j] = rope_bf16x8(kv[j], a.rope + (size_t)(pj * kPage + row) * (kHeadDim / 2) + ch * 4);
+        if (row >= valid)
+          kv[j] = make_uint4(0u, 0u, 0u, 0u);
+        else if (a.rope != nullptr)
+          kv[j] = rope_bf16x8(kv[j], cs[j]);
         *reinterpret_cast<uint4*>(&lds[j][swz(row, ch)]) = kv[j];
       }
     }
@@ -1410,8 +1456,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
 // copies its V page slot-major into an LDS tile of its own and reads it with
 // the transposing LDS read (GCA_WS_VROW=0: transposes it through registers
 // instead), then computes its page's scores, their softmax against its own
-// row max and the PV product.
-// The waves' (m, l, O) are combined in LDS in fp32.  Nothing passes through
+// row max and the PV product.  The V copies are issued last and waited for
+// only before the PV product.  The waves' (m, l, O) are combined in LDS in fp32.
+// kRope: the calls with rotary angles (Q and K rotated as their fragments
+// are read from LDS).  Nothing passes through
 // memory between these steps and there is no merge launch, so a lone frame
 // costs one short launch: the latency-bound case (one frame per call) that
 // the page-pipelined frame kernel, built for many frames, does not serve well.
@@ -1426,6 +1474,7 @@ constexpr int kWsExBytes = kAttnWaves * kWsRows * kWsPad * 4;
 static_assert(kWsExBytes <= kWsTilesBytes, "the O exchange fits in the tiles' space");
 
 
+template <bool kRope>
 __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs a_in) {
   const AttnArgs a = batch_frame<2>(a_in);
   constexpr int D = kHeadDim;
@@ -1452,23 +1501,28 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
   // repeat its last row; their outputs are not stored), every wave with keys
   // its K page (rows past the valid ones repeat the last valid row: their
   // scores are masked)
+  uint4 vr[8];
+  const int cg = lane >> 3, ch = lane & 7;
+  if (valid > 0 && GCA_WS_VROW) {  // uniform; rows past the valid ones repeat the last (P is 0 there)
+    // K first, then the Q block, then V: QK^T and the softmax start once
+    // the first two have landed, while V is still on its way
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      copy_rows8(kt_of(wave), i * 8, lane, [&](int r) {
+        return kin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
+      });
+  }
   if (wave < kWsRows / 8)
     copy_rows8(qt, wave * 8, lane, [&](int r) {
       const int row = min(qb * kWsRows + r, a.Lq - 1);
       return qin + ((size_t)row * H + h) * D;
     });
-  uint4 vr[8];
-  const int cg = lane >> 3, ch = lane & 7;
-  if (valid > 0 && GCA_WS_VROW) {  // uniform; rows past the valid ones repeat the last (P is 0 there)
+  if (valid > 0 && GCA_WS_VROW) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      copy_rows8(kt_of(wave), i * 8, lane, [&](int r) {
-        return kin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
-      });
+    for (int i = 0; i < 8; ++i)
       copy_vrows8(vt_of(wave), i * 8, lane, [&](int r) {
         return vin + ((size_t)(key0 + min(r, valid - 1)) * H + h) * D;
       });
-    }
   } else if (valid > 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -1499,16 +1553,27 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
       *reinterpret_cast<uint4*>(&vt[swz(ch * 8 + e, cg)]) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
     }
   }
-  GCA_WAIT_VMCNT(0);  // this wave's copies have landed
-  __syncthreads();    // and every wave's: the Q tile comes from waves 0-3
+  if (GCA_WS_VROW && valid > 0)
+    GCA_WAIT_VMCNT(8);  // this wave's K and Q copies have landed (its eight V copies may not)
+  else
+    GCA_WAIT_VMCNT(0);  // this wave's copies have landed
+  // and every wave's: the Q tile comes from waves 0-3.  Before this point
+  // only copies write the LDS (with GCA_WS_VROW), so the barrier needs no
+  // fence, whose wait would also hold the V copies
+  if constexpr (GCA_WS_VROW != 0)
+    wg_barrier();
+  else
+    __syncthreads();
 
-  // Q^T fragments: query row qb*32 + l32, d = 16c + 8hf .. +7
+  // Q^T fragments: query row qb*32 + l32, d = 16c + 8hf .. +7 (the angles
+  // are loaded here, where they are used: loading them with the copies
+  // measured 10 % slower)
   const int qrow = qb * kWsRows + l32;
   bf16x8 qf[1][4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     uint4 v = *reinterpret_cast<const uint4*>(&qt[swz(l32, c * 2 + hf)]);
-    if (a.rope != nullptr && qrow < a.Lq) v = rope_bf16x8(v, a.rope + (size_t)qrow * (D / 2) + c * 8 + hf * 4);
+    if (kRope && qrow < a.Lq) v = rope_bf16x8(v, a.rope + (size_t)qrow * (D / 2) + c * 8 + hf * 4);
     qf[0][c] = __builtin_bit_cast(bf16x8, v);
   }
 
@@ -1529,8 +1594,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
         // K fragment: key 32kt + l32 of the page, d = 16c + 8hf .. +7
         const int key = kt * 32 + l32;
         uint4 kv = *reinterpret_cast<const uint4*>(&kt_[swz(key, c * 2 + hf)]);
-        if (a.rope != nullptr && key < valid)
-          kv = rope_bf16x8(kv, a.rope + (size_t)(key0 + key) * (D / 2) + c * 8 + hf * 4);
+        if (kRope && key < valid) kv = rope_bf16x8(kv, a.rope + (size_t)(key0 + key) * (D / 2) + c * 8 + hf * 4);
         sc[kt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[0][c],
                                                             c == 0 ? zero : sc[kt][0], 0, 0, 0);
       }
@@ -1561,6 +1625,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_wsplit_bf16(AttnArgs 
     // O^T += V^T P^T: fragment i is d-tile i % 2, 16-key chunk i / 2
     const uint16_t* vt = vt_of(wave);
     const int vo[2] = {vrow_offset(0, lane), vrow_offset(1, lane)};
+    GCA_WAIT_VMCNT(0);  // this wave's V copies (read by this wave only)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       bf16x8 vf;
@@ -2111,7 +2176,10 @@ hipError_t launch_frame_wsplit(const AttnArgs& a, hipStream_t st) {
   if (a.batch < 1 || a.nsplit != 1 || a.pl.ppf < 1 || a.pl.ppf > kAttnWaves || a.Lq != a.F || a.H < 1)
     return hipErrorInvalidValue;
   const dim3 g3(a.H * ((a.Lq + kWsRows - 1) / kWsRows), a.batch);
-  hipLaunchKernelGGL(k_frame_wsplit_bf16, g3, dim3(kAttnWaves * 64), 0, st, a);
+  if (a.rope != nullptr)
+    hipLaunchKernelGGL(k_frame_wsplit_bf16<true>, g3, dim3(kAttnWaves * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_frame_wsplit_bf16<false>, g3, dim3(kAttnWaves * 64), 0, st, a);
   return hipGetLastError();
 }
 
