@@ -69,12 +69,16 @@ def test_stream_with_rotary(mode, M, H, k, T):
     stack.close()
 
 
-@pytest.mark.parametrize("mode,B", [("bf16", 3), ("bf16", 6), ("bf16", 70), ("fp32", 3)])
-def test_frame_attention_with_rotary(mode, B):
-    """3 bf16 frames: one page per wave; 6 and 70 (a full launch of 64 frames,
-    then 6): each frame held in LDS; fp32: scratch pages."""
+@pytest.mark.parametrize("mode,B,M", [("bf16", 3, 250), ("bf16", 6, 250), ("bf16", 70, 250), ("fp32", 3, 250),
+                                      ("bf16", 1, 181), ("bf16", 4, 447), ("bf16", 7, 181), ("bf16", 5, 500),
+                                      ("bf16", 2, 40), ("bf16", 6, 40)])
+def test_frame_attention_with_rotary(mode, B, M):
+    """1-4 bf16 frames: one page per wave; 5 and more (70: a full launch of 64
+    frames, then 6): each frame held in LDS; fp32: scratch pages.  M = 250
+    fills 4 whole pages; 181 and 447 end in a partial page (3 and 8 pages),
+    500 fills 8 pages with a partial last one, 40 a single partial page."""
     gdt, tdt = DT[mode]
-    M, S, H = 250, 6, 4
+    S, H = 6, 4
     F = M + S
     cfg = G.make_config(num_heads=H, image_tokens=M, summary_tokens=S, n_anchor=3, k_window=2,
                         max_frames=8, dtype=gdt)
