@@ -603,9 +603,9 @@ int gca_frame_attention(gca_ctx* c, const void* q, const void* k, const void* v,
   int rc = GCA_OK;
   // several frames: batches of up to fa_batch frames, one launch each (frame f
   // of a batch on grid row f, over its own scratch pages); a lone frame: the
-  // split-K path over ppf pages
-  // a bf16 frame of at most kFrameTiles pages runs in the LDS-resident frame
-  // kernel, which needs no scratch pages: batches of up to kFrameBatchMax
+  // split-K path over ppf pages.
+  // bf16 frames of at most kFrameTiles pages need no scratch pages (their
+  // kernels read the input rows): batches of up to kFrameBatchMax
   const int batch_max = g.ppf <= kFrameTiles && c->cfg.dtype == GCA_BF16 ? kFrameBatchMax : g.fa_batch;
   for (int f = 0; f < frames && rc == GCA_OK;) {
     const int nb = std::min(batch_max, frames - f);

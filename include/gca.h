@@ -157,8 +157,9 @@ int gca_set_rotary(gca_ctx* ctx, const float* cos_sin);
  * layer's cache is read or changed.  Frames go in batches, one launch each.
  * bf16 frames of at most 8 pages: a call of up to 4 frames runs one page per
  * wave of a workgroup (32 query rows per workgroup, the waves' partial
- * softmax results combined in LDS: no scratch, no merge launch); larger calls
- * hold each frame in LDS, up to 64 frames per launch.  Longer frames and the
+ * softmax results combined in LDS: no scratch, no merge launch); larger calls,
+ * up to 64 frames per launch, run the GCA step's page loop over the frames'
+ * own rows (with rotary angles: each frame held whole in LDS).  Longer frames and the
  * fp32 mode go through scratch pages inside the workspace
  * (ceil(256 / (H * query blocks)) frames per launch, capped at 64; a lone
  * such frame splits its keys, then the merge).
