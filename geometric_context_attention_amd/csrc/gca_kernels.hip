@@ -587,7 +587,10 @@ __device__ __forceinline__ void raise_max(const f32x16 (&sc)[2][NJ], float (&m)[
 // values that occurred, P keeps bf16's relative precision.
 constexpr uint32_t kSumLimitBits = 0x47800000u;  // 2^16 as fp32 bits; inf and NaN compare above
 
-template <int NJ, bool kArgs = false>
+// kSkipFirst: skip the pass at the old max on a first page, whose P would
+// be discarded (the frame kernels, whose every item of a few pages starts
+// with a first page; a split of the stream has one among dozens).
+template <int NJ, bool kArgs = false, bool kSkipFirst = false>
 __device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
                                            f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4], bool first, float c2 = 0.f) {
   if constexpr (kArgs) {  // the exponent arguments, when the MFMA phase left them
@@ -599,10 +602,12 @@ __device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], float (&m)[NJ], 
         for (int r = 0; r < 16; ++r) sc[kt][j][r] = __builtin_fmaf(sc[kt][j][r], c2, -m[j]);
   }
   float psum[NJ], shift[NJ];
-  page_exp<NJ, false>(sc, shift, pf, psum);
   bool big = first;
+  if (!kSkipFirst || !first) {
+    page_exp<NJ, false>(sc, shift, pf, psum);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) big |= __builtin_bit_cast(uint32_t, psum[j]) > kSumLimitBits;
+    for (int j = 0; j < NJ; ++j) big |= __builtin_bit_cast(uint32_t, psum[j]) > kSumLimitBits;
+  }
   if (__any(big)) {
     raise_max<NJ>(sc, m, l, o, shift, first);
     page_exp<NJ, true>(sc, shift, pf, psum);
@@ -1170,7 +1175,18 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   // a workgroup's first page, and the PV of that page's MFMA phase
   // multiplies the zero P).
   auto switch_item = [&](const uint16_t* sv, int first) __attribute__((always_inline)) {
-    GCA_WAIT_VMCNT(0);  // the query rows, copied one page after the last switch
+    // the query rows, copied on the finished item's second page: the page
+    // copies issued after them (two on each of its later pages but this one)
+    // may stay in flight (the counter completes loads in order)
+    switch (npg) {
+      case 3: GCA_WAIT_VMCNT(2); break;
+      case 4: GCA_WAIT_VMCNT(4); break;
+      case 5: GCA_WAIT_VMCNT(6); break;
+      case 6: GCA_WAIT_VMCNT(8); break;
+      case 7: GCA_WAIT_VMCNT(10); break;
+      case 8: GCA_WAIT_VMCNT(12); break;
+      default: GCA_WAIT_VMCNT(0); break;
+    }
     int lq = l32, hq = hf;  // addresses computed here, not held across the loop
     asm volatile("" : "+v"(lq), "+v"(hq));
 #pragma unroll
@@ -1249,7 +1265,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
       if (GCA_PINGPONG) wg_barrier();
       pc.lap(5);
       if constexpr (!kFrame && GCA_STAGE_MFMA == 0) stage_ahead();
-      valu_phase<NJ, kA>(sc, m, l, o, pf, jj == item_start, c2);
+      valu_phase<NJ, kA, kFrame>(sc, m, l, o, pf, jj == item_start, c2);
       if (__builtin_expect(kPersist && !grp_a && jj + 1 == next_start && item + 1 < nitems, 0))
         switch_item(ring[kRing + S], jj + 1);
       pc.lap(4);
@@ -1435,7 +1451,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void k_frame_attn_bf16(AttnArgs a_
     mfma_phase<NJ, true, true>(lds[jj], lds[jj == 0 ? 2 * kFrameTiles : kFrameTiles + jj - 1], qf, pf, o, sc, m, c2,
                                valid, l32, hf, vo0, vo1);
     wg_barrier();
-    valu_phase<NJ>(sc, m, l, o, pf, jj == 0);
+    valu_phase<NJ, false, true>(sc, m, l, o, pf, jj == 0);
     wg_barrier();
   }
   mfma_phase<NJ, true, true>(nullptr, lds[kFrameTiles + np - 1], qf, pf, o, sc, m, c2, kPage, l32, hf, vo0, vo1);
