@@ -24,8 +24,14 @@ constexpr int kMaxFramePages = 32;  // pages of one frame passed by value (F <= 
 constexpr int kFrameTiles = 8;
 constexpr int kFrameBatchMax = 64;
 // Up to kWsplitBatchMax such frames per call run in a kernel that splits each
-// frame's pages over the waves of a workgroup (no key splits, no merge).
-constexpr int kWsplitBatchMax = 4;
+// frame's pages over the waves of a workgroup (no key splits, no merge); the
+// larger calls go to the frame mode of the page loop.  (-DGCA_WS_BATCH_MAX=n
+// moves the boundary; the default is where the frame mode became faster.)
+#ifndef GCA_WS_BATCH_MAX
+#define GCA_WS_BATCH_MAX 4
+#endif
+static_assert(GCA_WS_BATCH_MAX >= 1 && GCA_WS_BATCH_MAX <= 64, "a batch of the wave-split kernel fits its grid rows");
+constexpr int kWsplitBatchMax = GCA_WS_BATCH_MAX;
 
 // Device-side state of one layer's cache, carved from the workspace.
 struct LayerDev {
