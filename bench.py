@@ -366,12 +366,14 @@ def frame_attention_bench(args, cfg, G, torch, dev):
     L = G.lib()
     ctx = stack.ctx
     R = max(args.pool, B)
+    f32 = args.dtype == "fp32"
+    tdt = torch.float32 if f32 else torch.bfloat16
     pools = []
     for layer in range(Ly):
-        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=torch.bfloat16, seed=0, chunk=32)
+        spec = StreamSpec(H=H, D=D, M=M, S=S, dtype=tdt, seed=0, chunk=32)
         pools.append(draw_frames(spec, layer, 0, R, device=dev))
-    out = torch.empty((B, F, H, D), dtype=torch.bfloat16, device=dev)
-    fb = F * H * D * 2
+    out = torch.empty((B, F, H, D), dtype=tdt, device=dev)
+    fb = F * H * D * (4 if f32 else 2)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     fa = L.gca_frame_attention
@@ -382,10 +384,18 @@ def frame_attention_bench(args, cfg, G, torch, dev):
         G.gca_set_rotary(ctx, tab)
     # the kernel that runs the calls (see gca_frame_attention): up to 4 bf16
     # frames of <= 8 pages one page per wave, more of them through the
-    # pipelined page loop's frame mode (k_attn_bf16<8, true>)
+    # pipelined page loop's frame mode (k_attn_bf16<8, true>) or, with rotary
+    # angles, k_frame_attn_bf16; longer frames and fp32 over scratch pages
     ppf = -(-F // 64)
-    frame_kernel = ("k_frame_wsplit_bf16" if B <= 4 else ("k_frame_attn_bf16" if args.rotary else "k_attn_bf16 frame mode")
-                    if ppf <= 8 else "k_attn_bf16")
+    if f32:
+        frame_kernel = "k_attn_f32"
+    elif ppf > 8:
+        frame_kernel = "k_attn_bf16"
+    elif B <= 4:
+        frame_kernel = "k_frame_wsplit_bf16"
+    else:
+        frame_kernel = "k_frame_attn_bf16" if args.rotary else "k_attn_bf16 frame mode"
+    peak = PEAK_FP32_TFLOPS if f32 else PEAK_BF16_TFLOPS
 
     def run():
         for t, nb in calls:
@@ -419,18 +429,20 @@ def frame_attention_bench(args, cfg, G, torch, dev):
         log(f"phase cycles (workgroup 0 of the sampled launches): {json.dumps(phases)}")
     # Algorithmic bytes: every frame's Q, K and V read once and O written once
     # (no LSE here), i.e. twice the K/V bytes the profile counts.  At
-    # head_dim 64 and M+S = 506 that is 251 flop/byte, below the ridge of the
+    # head_dim 64 and M+S = 506 that is 253 flop/byte, below the ridge of the
     # bf16 peak over HBM (312.5 flop/byte): the roofline that bounds these
-    # layers is HBM, and the MFMA fraction is reported beside it.
+    # layers is HBM, and the MFMA fraction is reported beside it.  (Longer
+    # frames, and the fp32 peak, whose ridge is 19.7 flop/byte, are bound by
+    # the matrix cores.)
     launches = max(prof["attn_launches"], 1)
     io_bytes = 2.0 * prof["attn_kv_bytes"]
     intensity = prof["attn_flop"] / io_bytes if io_bytes > 0 else 0.0
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
     gbs = io_bytes / (prof["attn_ms"] * 1e-3) / 1e9 if prof["attn_ms"] > 0 else 0.0
     hbm_bound = intensity < ridge
-    attainable = min(PEAK_BF16_TFLOPS, PEAK_HBM_GBS * intensity / 1e3)
+    attainable = min(peak, PEAK_HBM_GBS * intensity / 1e3)
     result = {
-        "metric": "intra-frame attention frames/s (12 layers, M=500+6, H=16) + % of the roofline",
+        "metric": f"intra-frame attention frames/s ({Ly} layers, M={M}+{S}, H={H}) + % of the roofline",
         "value": round(fps, 2),
         "unit": "frames/s",
         "n_gpus": 1,
@@ -440,30 +452,31 @@ def frame_attention_bench(args, cfg, G, torch, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic (seeded N(0,1), resident pool of frames per layer)",
         "config": {"workload": f"intra-frame attention: {Ly} layers, H={H}, D={D}, M={M}+{S}, T={T} frames, "
-                               f"{B} frames per call, bf16" + (", rotary Q/K" if args.rotary else ""),
+                               f"{B} frames per call, {args.dtype}" + (", rotary Q/K" if args.rotary else ""),
                    "frames_per_call": B},
         "roofline": {
             "bound": "hbm" if hbm_bound else "mfma",
             "kernel": frame_kernel,
             "achieved": round(gbs, 1) if hbm_bound else round(achieved, 2),
-            "peak": PEAK_HBM_GBS if hbm_bound else PEAK_BF16_TFLOPS,
+            "peak": PEAK_HBM_GBS if hbm_bound else peak,
             "unit": "GB/s" if hbm_bound else "TFLOP/s",
-            "frac": round(gbs / PEAK_HBM_GBS, 4) if hbm_bound else round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(gbs / PEAK_HBM_GBS, 4) if hbm_bound else round(achieved / peak, 4),
             "traffic": (read_traffic(FRAME_TRAFFIC_FILE)
-                        if (B, T, Ly, H, M, S) == (64, 2048, 12, 16, 500, 6) and not args.rotary else None),
+                        if (B, T, Ly, H, M, S) == (64, 2048, 12, 16, 500, 6) and not args.rotary and not f32
+                        else None),
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "sampled_launches": prof["attn_launches"],
             "algorithmic_flop_per_launch": prof["attn_flop"] / launches,
             "algorithmic_bytes_per_launch": io_bytes / launches,
             "arithmetic_intensity_flop_per_byte": round(intensity, 1),
             "tflops": round(achieved, 2),
-            "frac_of_mfma_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac_of_mfma_peak": round(achieved / peak, 4),
             "frac_of_attainable": round(achieved / attainable, 4) if attainable > 0 else None,
             "clock_ghz": round(clock, 3),
-            "frac_at_clock": round(achieved / (PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
+            "frac_at_clock": round(achieved / (peak * clock / PEAK_CLOCK_GHZ), 4) if clock > 0 else None,
         },
     }
     stack.close()
