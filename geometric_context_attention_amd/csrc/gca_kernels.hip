@@ -76,15 +76,25 @@ __device__ __forceinline__ uint16_t f32_to_elem<uint16_t>(float x) { return __bu
 template <>
 __device__ __forceinline__ float f32_to_elem<float>(float x) { return x; }
 
-// Rotate a 16-byte chunk of 8 bf16 channels d0 .. d0+7 (pairs d0/2 ..) of one row.
-__device__ __forceinline__ uint4 rope_bf16x8(uint4 v, const float2* cs) {
+// Rotate a 16-byte chunk of 8 bf16 channels d0 .. d0+7 (pairs d0/2 ..) of one
+// row; with a factor `s` the rotated values are also multiplied by it, in
+// fp32, before the one rounding to bf16.
+__device__ __forceinline__ uint4 rope_bf16x8(uint4 v, const float2* cs, float s = 1.f) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
     rope_rotate(x0, x1, cs[e]);
-    w[e] = pack_bf16(x0, x1);
+    w[e] = pack_bf16(x0 * s, x1 * s);
   }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// 8 bf16 values times `s` (fp32 product, rounded to bf16)
+__device__ __forceinline__ uint4 scale_bf16x8(uint4 v, float s) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pack_bf16(bf16_lo(w[e]) * s, bf16_hi(w[e]) * s);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -326,6 +336,27 @@ static_assert(GCA_SOFT_EXP == 0 || GCA_SOFT_EXP == 4 || GCA_SOFT_EXP == 8, "a qu
 #define GCA_ASYM_ARGS 0
 #endif
 constexpr bool kAsymArgs = GCA_ASYM_ARGS != 0;
+// 1: the stream kernel multiplies Q by scale * log2 e before the QK^T
+// product (Q rounded to bf16 once more), so that the scores come out of the
+// matrix core in log2 units, and it subtracts a running max only once some
+// row of the wave needs one (see valu_phase_qs): the softmax then runs no
+// per-score arithmetic before the exponential.  0: every score is turned
+// into s * scale * log2 e - m by a multiply-add.
+#ifndef GCA_QSCALE
+#define GCA_QSCALE 0
+#endif
+// 1: the QK^T products of a page run d-chunk by d-chunk with the next
+// chunk's K fragments read one chunk ahead; 0: key tile by key tile, each
+// fragment read just before its two products.
+#ifndef GCA_KPREFETCH
+#define GCA_KPREFETCH 0
+#endif
+// Independent accumulator chains of a lane's row sum over a page (1, 2 or 4)
+#ifndef GCA_SUM_CHAINS
+#define GCA_SUM_CHAINS 1
+#endif
+constexpr int kSumChains = GCA_SUM_CHAINS;
+static_assert(kSumChains == 1 || kSumChains == 2 || kSumChains == 4, "1, 2 or 4 chains");
 // Intra-frame attention without rotary angles through the pipelined page
 // loop (frame mode of k_attn_bf16) instead of k_frame_attn_bf16.
 #ifndef GCA_FRAME_RING
@@ -520,7 +551,8 @@ __device__ __forceinline__ constexpr bool soft_exp_slot(int r) {
 
 // p = exp2(x - shift) as packed bf16 P^T fragments (pf[j][kc]: 16-key chunk
 // kc of the page); psum[j] is the sum of the same rounded values over this
-// lane's 32 keys (v_dot2 with (1, 1)).
+// lane's 32 keys (v_dot2 with (1, 1), in kSumChains independent
+// accumulator chains added pairwise at the end).
 template <int NJ, bool kShift>
 __device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float (&shift)[NJ],
                                          bf16x8 (&pf)[NJ][4], float (&psum)[NJ]) {
@@ -534,15 +566,22 @@ __device__ __forceinline__ void page_exp(const f32x16 (&sc)[2][NJ], const float 
         const float x = kShift ? sc[kt][j][r] - shift[j] : sc[kt][j][r];
         pf[j][kt * 2 + (r >> 3)][r & 7] = (__bf16)(soft_exp_slot(r) ? exp2_poly(x) : __builtin_amdgcn_exp2f(x));
       }
-    float acc = 0.f;
+    float acc[kSumChains];
+#pragma unroll
+    for (int t = 0; t < kSumChains; ++t) acc[t] = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const bf16x2 pr = {pf[j][kc][e], pf[j][kc][e + 1]};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+        const int t = (kc * 4 + e / 2) % kSumChains;
+        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc[t], false);
       }
-    psum[j] = acc;
+#pragma unroll
+    for (int w = 1; w < kSumChains; w *= 2)
+#pragma unroll
+      for (int t = 0; t < kSumChains; t += 2 * w) acc[t] += acc[t + w];
+    psum[j] = acc[0];
   }
 }
 
@@ -611,6 +650,46 @@ __device__ __forceinline__ void valu_phase(f32x16 (&sc)[2][NJ], float (&m)[NJ], 
   if (__any(big)) {
     raise_max<NJ>(sc, m, l, o, shift, first);
     page_exp<NJ, true>(sc, shift, pf, psum);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) l[j] += psum[j];
+}
+
+// VALU phase of the stream kernel when Q was multiplied by scale * log2 e
+// before the QK^T product: a score is already in log2 units.  Every row's
+// max starts at 0 and is left there while the split's first page gives each
+// lane a sum (over its 32 keys) in [2^-20, 2^16] and no later page gives one
+// above 2^16; the exponent argument is then the score itself.  Otherwise the
+// max is raised as in valu_phase (on the first page: set to the page's row
+// max), and from then on (`eng`, wave-uniform) the wave subtracts it from
+// every score.  Every p stays at most 2^16 and, after the first page, every
+// row sum at least 2^-20, so neither the sums overflow nor the rows that
+// keep a zero max lose their weight to underflow.
+constexpr uint32_t kSumFloorBits = 0x35800000u;  // 2^-20
+
+template <int NJ>
+__device__ __forceinline__ void valu_phase_qs(f32x16 (&sc)[2][NJ], float (&m)[NJ], float (&l)[NJ],
+                                              f32x16 (&o)[2][NJ], bf16x8 (&pf)[NJ][4], bool first, bool& eng) {
+  if (eng) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kt][j][r] -= m[j];
+  }
+  float psum[NJ], shift[NJ];
+  page_exp<NJ, false>(sc, shift, pf, psum);
+  bool out = false;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint32_t b = __builtin_bit_cast(uint32_t, psum[j]);
+    out |= b > kSumLimitBits || (first && b < kSumFloorBits);
+  }
+  if (__any(out)) {
+    raise_max<NJ>(sc, m, l, o, shift, first);
+    page_exp<NJ, true>(sc, shift, pf, psum);
+    eng = true;
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) l[j] += psum[j];
@@ -701,15 +780,43 @@ __device__ __forceinline__ void mfma_phase(const uint16_t* sk, const uint16_t* s
                                            int vo0 = 0, int vo1 = 0, const AfterV& after_v = AfterV{}) {
   if (sk != nullptr) {
     const f32x16 zero = {};
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int row = kt * 32 + l32;
+    if constexpr (GCA_KPREFETCH) {
+      // d-chunk outer, key tile inner: the two K fragments of chunk c + 1
+      // are read right after the first of the four products of chunk c,
+      // so each read lands behind three MFMAs, and no read is younger than
+      // the ones the next wait is for
+      auto kfrag = [&](int kt, int c) {
+        return *reinterpret_cast<const bf16x8*>(&sk[swz(kt * 32 + l32, c * 2 + hf)]);
+      };
+      bf16x8 kb[2][2] = {{kfrag(0, 0), kfrag(1, 0)}, {}};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[swz(row, c * 2 + hf)]);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          sc[kt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[kt][j], 0, 0, 0);
+        for (int u = 0; u < 2 * NJ; ++u) {
+          const int kt = u / NJ, j = u % NJ;
+          sc[kt][j] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[c % 2][kt], qf[j][c], c == 0 ? zero : sc[kt][j], 0, 0, 0);
+          // the scheduler would otherwise sink the reads next to their use
+          // to save registers
+          if (u == 0 && c + 1 < 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            kb[(c + 1) % 2][0] = kfrag(0, c + 1);
+            kb[(c + 1) % 2][1] = kfrag(1, c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kt * 32 + l32;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sk[swz(row, c * 2 + hf)]);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            sc[kt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[j][c], c == 0 ? zero : sc[kt][j], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -849,8 +956,9 @@ __device__ __forceinline__ void for_each_slot(int jj, int np, F& f) {
 }
 
 // Q^T fragments of a bf16 attention workgroup: tile j, d-chunk c: column
-// q = 32j + l32, d = 16c + 8hf .. +7 (rotated when rotary angles are given).
-template <int NJ>
+// q = 32j + l32, d = 16c + 8hf .. +7 (rotated when rotary angles are given;
+// kScale: times scale * log2 e, rounded to bf16 once).
+template <int NJ, bool kScale = false>
 __device__ __forceinline__ void load_q(const AttnArgs& a, bf16x8 (&qf)[NJ][4], int h, int qb, int wave, int l32,
                                        int hf) {
   constexpr int D = kHeadDim;
@@ -863,7 +971,10 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, bf16x8 (&qf)[NJ][4], i
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (row < a.Lq) {
         v = *reinterpret_cast<const uint4*>(qbase + ((size_t)row * a.H + h) * D + c * 16 + hf * 8);
-        if (a.rope != nullptr) v = rope_bf16x8(v, a.rope + (size_t)row * (D / 2) + c * 8 + hf * 4);
+        if (a.rope != nullptr)
+          v = rope_bf16x8(v, a.rope + (size_t)row * (D / 2) + c * 8 + hf * 4, kScale ? a.scale_log2 : 1.f);
+        else if (kScale)
+          v = scale_bf16x8(v, a.scale_log2);
       }
       qf[j][c] = __builtin_bit_cast(bf16x8, v);
     }
@@ -992,6 +1103,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   static_assert(NW == 8, "the staging layout assumes 512 threads");
   constexpr int NJ = 2;
   constexpr int D = kHeadDim;
+  constexpr bool kQS = GCA_QSCALE != 0 && !kFrame;  // Q pre-scaled, see valu_phase_qs
   // One LDS array holds the ring (tiles 0 .. 2*kRing-1) and the page list
   // (the tiles after it): with a single LDS object the compiler can tell the
   // ring slots apart and waits on the copies only where this code asks it to.
@@ -1041,7 +1153,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
   if constexpr (kFrame)
     load_q<NJ>(frame_of<2>(a, fcur), qf, h, qb, wave, l32, hf);
   else
-    load_q<NJ>(a, qf, h, qb, wave, l32, hf);
+    load_q<NJ, kQS>(a, qf, h, qb, wave, l32, hf);
   pc.lap(0);
 
   const int f0 = npg - a.pl.fresh_cnt;  // first page of the appended frame
@@ -1122,6 +1234,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     l[j] = 0.f;
   }
   const float c2 = a.scale_log2;
+  bool eng = false;  // some row of this wave has a nonzero max (kQS)
 
   // Ping-pong.  Every wave runs the same per-page sequence -- an MFMA phase
   // (QK^T of page j, then PV of page j-1 beside the exponent arguments of page
@@ -1256,16 +1369,19 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
         mfma_phase<NJ, !kA, true>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
                                   (int)(ent[S] & 127u), l32, hf, vo0, vo1, stage_ahead);
       else if constexpr (GCA_STAGE_MFMA != 0)
-        mfma_phase<NJ, !kA, false>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
-                                   (int)(ent[S] & 127u), l32, hf, 0, 0, stage_ahead);
+        mfma_phase<NJ, !kA && !kQS, false>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                                           (int)(ent[S] & 127u), l32, hf, 0, 0, stage_ahead);
       else
-        mfma_phase<NJ, !kA>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
-                            (int)(ent[S] & 127u), l32, hf);
+        mfma_phase<NJ, !kA && !kQS>(ring[S], ring[kRing + (S + kRing - 1) % kRing], qf, pf, o, sc, m, c2,
+                                    (int)(ent[S] & 127u), l32, hf);
       pc.lap(3);
       if (GCA_PINGPONG) wg_barrier();
       pc.lap(5);
       if constexpr (!kFrame && GCA_STAGE_MFMA == 0) stage_ahead();
-      valu_phase<NJ, kA, kFrame>(sc, m, l, o, pf, jj == item_start, c2);
+      if constexpr (kQS)
+        valu_phase_qs<NJ>(sc, m, l, o, pf, jj == item_start, eng);
+      else
+        valu_phase<NJ, kA, kFrame>(sc, m, l, o, pf, jj == item_start, c2);
       if (__builtin_expect(kPersist && !grp_a && jj + 1 == next_start && item + 1 < nitems, 0))
         switch_item(ring[kRing + S], jj + 1);
       pc.lap(4);
@@ -1280,7 +1396,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a_in) {
     };
     for (int jj = 0; jj < np; jj += kRing) for_each_slot<0, kRing>(jj, np, page_step);
   };
-  if (kAsymArgs && grp_a)
+  if (kAsymArgs && !kQS && grp_a)
     run_pages(std::true_type{});
   else
     run_pages(std::false_type{});
