@@ -41,10 +41,29 @@ def build(verbose: bool = False, defines=(), name: str = "libgca.so") -> str:
     return lib
 
 
+PROBE_SRC = os.path.join(CSRC, "issue_rate_probe.hip")
+PROBE = os.path.join(PKG, "issue_rate_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the VALU/MFMA issue-rate probe (a diagnostic executable)."""
+    tmp = PROBE + ".tmp"
+    cmd = [HIPCC, *DEVICE_FLAGS, PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build the issue-rate probe")
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser()
     ap.add_argument("-D", dest="defines", action="append", default=[], help="extra define, e.g. GCA_SOFT_EXP=4")
     ap.add_argument("--name", default="libgca.so", help="library file name in the package directory")
+    ap.add_argument("--probe", action="store_true", help="build the issue-rate probe executable instead")
     a = ap.parse_args()
-    print(build(verbose=True, defines=a.defines, name=a.name))
+    print(build_probe(verbose=True) if a.probe else build(verbose=True, defines=a.defines, name=a.name))
