@@ -24,7 +24,7 @@ DT = {"bf16": (G.GCA_BF16, torch.bfloat16), "fp32": (G.GCA_FP32, torch.float32)}
 
 def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scale=1.0,
                 state_every=1, check_bytes=True, key_offset_std=0.0, interval=1, chosen=None,
-                pool_pages=0):
+                pool_pages=0, k_boost=()):
     """Stream T frames through every layer; compare each step with the oracle."""
     gdt, tdt = DT[mode]
     F = M + S
@@ -41,6 +41,8 @@ def _run_stream(mode, M, n, k, T, H, S=6, seed=0, layers=1, max_splits=0, q_scal
         q, kx, v = draw_frames(spec, layer, 0, T)  # CPU generator: [T, F, H, D]
         if q_scale != 1.0:
             q = (q.float() * q_scale).to(tdt)
+        for f, r, h, fac in k_boost:  # powers of two: exact in either dtype
+            kx[f, r, h] = (kx[f, r, h].float() * fac).to(tdt)
         o_ref, l_ref = go.stream_online(to64(q), to64(kx), to64(v), shp, scale)
         qd, kd, vd = q.cuda(), kx.cuda(), v.cuda()
         pm = PageModel(n=n, k=k, F=F, S=S, P=64, num_pages=G.gca_plan(cfg, 0)["pool_pages"],
@@ -119,6 +121,17 @@ def test_bf16_edge_shapes(M, n, k, T, H):
 def test_bf16_sharpened_queries():
     """Q scaled by 4 makes the softmax peaked (|O| ~ 1), so the max-abs gate bites."""
     _run_stream("bf16", M=120, n=3, k=4, T=24, H=2, q_scale=4.0, state_every=8, check_bytes=False)
+
+
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_outlier_keys_raise_the_max(mode):
+    """A few key rows scaled by 64 score up to ~200 (natural units) above
+    the rest: on the pages that hold them the exponentials at the running
+    max overflow, and the max has to be raised mid-split.  One of them is a
+    summary row, so it stays in trajectory memory after its frame leaves
+    the window."""
+    boost = ((4, 2, 0, 64.0), (9, 70, 1, 64.0), (15, 33, 0, 64.0), (19, 5, 1, 64.0))
+    _run_stream(mode, M=120, n=3, k=4, T=24, H=2, k_boost=boost, state_every=8, check_bytes=False)
 
 
 def test_fp32_correlated_keys():
