@@ -255,6 +255,19 @@ def test_bf16_keyframe_interval_ragged():
     _run_stream("bf16", M=181, n=2, k=3, T=40, H=4, interval=2, state_every=5)
 
 
+@pytest.mark.parametrize("mode", ["bf16", "fp32"])
+def test_variants_combined(mode):
+    """Keyframe interval 2, two summary tokens and a single anchor frame
+    together, with ragged frames (M + S = 83), state every step."""
+    _run_stream(mode, M=81, n=1, k=3, T=30, H=3, S=2, interval=2, state_every=1)
+
+
+def test_bf16_many_heads():
+    """96 heads: fewer key splits per head than pages, one split for some
+    steps, the grid still filling the chip."""
+    _run_stream("bf16", M=40, n=2, k=3, T=14, H=96, state_every=4)
+
+
 def test_bf16_caller_chosen_keyframes():
     """Keyframes chosen per step by the caller (gca_step_keyframe), bf16, state checks."""
     rng = np.random.default_rng(5)
